@@ -1,0 +1,142 @@
+/*
+ * libaxonscan — C ABI of the selective-scan hot path of the Axon-SSM layer on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * What is computed. The pages cited below are:
+ *   [AXON] "Axon-SSM: Selective State Space Model for Apple Silicon" (bit-axon docs).
+ *   [WIKI] "Selective State Space Models (Mamba)" (wiki note, "Selective scan (toy)" and
+ *          "1M context inference" patterns).
+ *
+ * For every batch row b and channel e (d_inner = E channels) the layer carries a state
+ * h[b,e,0..N-1] and runs, for t = 0..L-1:
+ *
+ *   u_t   = conv_b[e] + sum_{k=0}^{K-1} conv_w[e,k] * xx[t-(K-1)+k]
+ *             [AXON "Key contributions": causal depthwise conv1d, kernel size 4, before the scan;
+ *              xx[s] = x[b,s,e] for s >= 0, taken from conv_cache for s < 0]
+ *   dt_t  = min(max(softplus(dt_raw[b,t,e] + dt_bias[e]), dt_min), dt_max)
+ *             [AXON "Selective mechanism": softplus of the raw step plus a bias, clipped to
+ *              [eps, dt_max] with eps = 1e-4, dt_max = 100]
+ *   A_n   = -exp(A_log[e,n])                       [AXON "Diagonal state matrix"]
+ *   h_n  <- exp(dt_t * A_n) * h_n + dt_t * B[b,t,n] * u_t
+ *             [AXON "ZOH discretization": first-order form, Abar = exp(dt A), Bbar = dt B]
+ *   y_t   = sum_n C[b,t,n] * h_n + D[e] * u_t      [AXON "Continuous-time SSM", readout]
+ *   out[b,t,e] = y_t * z_t * sigmoid(z_t)          [AXON "Gating": y times SiLU(z)]
+ *
+ * There is no activation between the convolution and the scan (the Axon-SSM page applies SiLU
+ * only on the z branch). B, C and dt_raw arrive already projected; the projections W_in,
+ * f_proj and W_out are the caller's.
+ *
+ * Layouts (all row-major, contiguous, innermost index last):
+ *   x, z, dt_raw, y : (batch, seqlen, d_inner), activation dtype
+ *   B, C            : (batch, seqlen, d_state), activation dtype
+ *   A_log           : (d_inner, d_state) fp32
+ *   D, dt_bias      : (d_inner) fp32
+ *   conv_w          : (d_inner, d_conv) fp32; tap d_conv-1 multiplies the current token
+ *   conv_b          : (d_inner) fp32
+ *   conv_cache      : (batch, d_conv-1, d_inner) fp32; the last d_conv-1 x-branch inputs seen
+ *                     (before the convolution), oldest first [AXON "Autoregressive decoding"]
+ *   ssm_state       : (batch, d_inner, d_state) fp32 [AXON "Autoregressive decoding"]
+ *
+ * Supported shapes: d_state == 16, d_conv == 4 (the layer configuration table of [AXON]);
+ * batch >= 1, d_inner >= 1, seqlen >= 0; batch*seqlen*d_inner < 2^62.
+ * Activation dtype: fp32 or bf16 (bf16 outputs are rounded to nearest even from fp32).
+ * State, cache and parameters are always fp32; the state recurrence runs in fp32.
+ *
+ * Ownership and memory: every tensor pointer is device memory owned by the caller, 16-byte
+ * aligned. The library allocates nothing and keeps no mutable global state; scratch memory
+ * is a caller-provided workspace. Calls are asynchronous on the given stream (a hipStream_t
+ * passed as void*; NULL = the default stream); nothing is synchronised on the host.
+ *
+ * Errors: every argument is checked on the host before anything is launched. On any error
+ * code other than AXON_ERR_HIP nothing has been enqueued and no memory was written.
+ * AXON_ERR_HIP means a launch failed (hipGetLastError); outputs are then unspecified.
+ * The functions are thread-safe.
+ */
+#ifndef AXONSCAN_H_
+#define AXONSCAN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AXON_OK = 0,
+  AXON_ERR_INVALID_ARGUMENT = 1,  /* null/misaligned pointer, bad size, forbidden aliasing */
+  AXON_ERR_UNSUPPORTED = 2,       /* d_state != 16, d_conv != 4, unknown dtype */
+  AXON_ERR_WORKSPACE_TOO_SMALL = 3,
+  AXON_ERR_HIP = 4                /* a HIP launch or runtime call failed */
+} axon_status;
+
+typedef enum { AXON_F32 = 0, AXON_BF16 = 1 } axon_dtype;
+
+typedef struct {
+  int64_t batch;      /* B */
+  int64_t seqlen;     /* L (ignored by the decode step) */
+  int64_t d_inner;    /* E, channels */
+  int64_t d_state;    /* N, must be 16 */
+  int64_t d_conv;     /* K, must be 4 */
+  axon_dtype act_dtype;
+} axon_ssm_shape;
+
+typedef struct {
+  const float* A_log;    /* (E, N) */
+  const float* D;        /* (E)    */
+  const float* dt_bias;  /* (E)    */
+  const float* conv_w;   /* (E, K) */
+  const float* conv_b;   /* (E)    */
+  float dt_min;          /* lower clip of dt; the Axon-SSM page uses 1e-4 */
+  float dt_max;          /* upper clip of dt; the Axon-SSM page uses 100  */
+} axon_ssm_params;
+
+/* Library version as 10000*major + 100*minor + patch. */
+int axon_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* axon_status_string(axon_status status);
+
+/* Bytes of device workspace axon_ssm_prefill needs for this shape (0 is possible). A pure
+ * function of the shape: no device is queried. Returns 0 for an invalid shape as well, so call
+ * axon_ssm_prefill for the diagnosis. */
+size_t axon_ssm_prefill_workspace_bytes(const axon_ssm_shape* shape);
+
+/* Prefill: runs the layer over seqlen tokens for every (b, e), continuing from the given cache.
+ *
+ * conv_cache_in (B, K-1, E) and ssm_state_in (B, E, N) may be NULL, meaning zeros (a fresh
+ * sequence, as with state = None in the streaming loop of [WIKI "1M context inference"]).
+ * conv_cache_out and ssm_state_out receive the cache after the last token; they may be equal to
+ * the corresponding inputs (in-place update) but must not partially overlap them. y must not
+ * overlap any input. Prefill(L1) followed by prefill(L2) from its caches equals prefill(L1+L2)
+ * up to rounding.
+ * seqlen == 0 copies the caches in to out unchanged (zeros for NULL inputs) and writes no y.
+ * The conv cache after the call holds exact copies (fp32, exact widening for bf16) of the last
+ * K-1 x-branch inputs of the concatenation [cache_in, x].
+ * workspace: device memory of at least axon_ssm_prefill_workspace_bytes(shape) bytes, 16-byte
+ * aligned; may be NULL when that size is 0. Its contents need no initialisation. */
+axon_status axon_ssm_prefill(const axon_ssm_shape* shape, const axon_ssm_params* params,
+                             const void* x, const void* z, const void* dt_raw,
+                             const void* B, const void* C,
+                             const float* conv_cache_in, const float* ssm_state_in,
+                             void* y, float* conv_cache_out, float* ssm_state_out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode step: one token per batch row, with the caches updated in place
+ * [AXON "Autoregressive decoding": the cache pair carries the convolution padding and the
+ * hidden state from one step to the next].
+ * x, z, dt_raw, y: (B, E) activation dtype; B, C: (B, N) activation dtype;
+ * conv_cache (B, K-1, E) and ssm_state (B, E, N) fp32, read and then overwritten.
+ * shape->seqlen is ignored. y must not overlap any input or cache. Equivalent to
+ * axon_ssm_prefill with seqlen = 1 and in-place caches. */
+axon_status axon_ssm_decode_step(const axon_ssm_shape* shape, const axon_ssm_params* params,
+                                 const void* x, const void* z, const void* dt_raw,
+                                 const void* B, const void* C,
+                                 float* conv_cache, float* ssm_state,
+                                 void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AXONSCAN_H_ */

@@ -1,0 +1,67 @@
+/*
+ * CPU oracle of the Axon-SSM selective-scan hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark load this code. The product path (libaxonscan) never links, loads or calls it, and
+ * the two share no source, header or helper.
+ *
+ * Every value is widened to double on entry and every result is returned in double, so that
+ * rounding in the oracle stays far below the tolerances it is compared against. The arithmetic
+ * is the plain definition, evaluated one token at a time in the order the pages give it.
+ */
+#ifndef AXON_ORACLE_H_
+#define AXON_ORACLE_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* One channel (one (b, e) pair) over L tokens.
+ *   x, z, dt_raw : token t at [t * act_stride]
+ *   Bm, Cm       : B_t,n at [t * bc_stride + n]
+ *   A_log        : N values; conv_w: K values, conv_w[K-1] multiplies the current token
+ *   win_in       : the K-1 x-branch inputs that precede token 0, oldest first; NULL = zeros
+ *   h_in         : N initial states; NULL = zeros
+ *   y            : output token t at [t * y_stride]
+ *   win_out      : K-1 values, the last K-1 x-branch inputs of [win_in, x], oldest first
+ *   h_out        : N final states
+ *   u_out, dt_out: optional (may be NULL) per-token conv output and step size, [t * y_stride]
+ * Returns 0, or -1 for an invalid argument. */
+int oracle_ssm_channel(int64_t L, int64_t N, int64_t K,
+                       const float* x, const float* z, const float* dt_raw, int64_t act_stride,
+                       const float* Bm, const float* Cm, int64_t bc_stride,
+                       const float* A_log, double D, double dt_bias, const float* conv_w,
+                       double conv_b, double dt_min, double dt_max,
+                       const double* win_in, const double* h_in,
+                       double* y, int64_t y_stride, double* win_out, double* h_out,
+                       double* u_out, double* dt_out);
+
+/* Whole prefill over (B, L, E) tensors laid out as in libaxonscan's header:
+ *   x, z, dt_raw (B,L,E); Bm, Cm (B,L,N); A_log (E,N); D, dt_bias, conv_b (E); conv_w (E,K);
+ *   conv_cache_in (B,K-1,E) or NULL; ssm_state_in (B,E,N) or NULL;
+ *   y (B,L,E); conv_cache_out (B,K-1,E); ssm_state_out (B,E,N).
+ * threads >= 1 splits the independent channels over that many POSIX threads. */
+int oracle_ssm_prefill(int64_t Bsz, int64_t L, int64_t E, int64_t N, int64_t K,
+                       const float* x, const float* z, const float* dt_raw,
+                       const float* Bm, const float* Cm,
+                       const float* A_log, const float* D, const float* dt_bias,
+                       const float* conv_w, const float* conv_b, double dt_min, double dt_max,
+                       const double* conv_cache_in, const double* ssm_state_in,
+                       double* y, double* conv_cache_out, double* ssm_state_out, int threads);
+
+/* One decode step: x, z, dt_raw (B,E); Bm, Cm (B,N); conv_cache (B,K-1,E) and ssm_state (B,E,N)
+ * are read and overwritten; y (B,E). */
+int oracle_ssm_decode_step(int64_t Bsz, int64_t E, int64_t N, int64_t K,
+                           const float* x, const float* z, const float* dt_raw,
+                           const float* Bm, const float* Cm,
+                           const float* A_log, const float* D, const float* dt_bias,
+                           const float* conv_w, const float* conv_b, double dt_min, double dt_max,
+                           double* conv_cache, double* ssm_state, double* y, int threads);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AXON_ORACLE_H_ */

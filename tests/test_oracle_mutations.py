@@ -1,0 +1,68 @@
+"""Planted mistakes: each variant of the oracle below carries one plausible error (a dropped
+term, a wrong sign, a transposed operand, a wrong index). Every variant is compiled on the CPU
+and must fail at least one pin, which shows the pins can see that kind of mistake."""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "axon_oracle.c")
+
+MUTATIONS = {
+    "drop_D_skip": ("acc += D * u;", "acc += 0.0 * D * u;"),
+    "positive_A": ("A[n] = -exp((double)A_log[n]);", "A[n] = exp((double)A_log[n]);"),
+    "A_without_exp": ("A[n] = -exp((double)A_log[n]);", "A[n] = -(double)A_log[n];"),
+    "bbar_without_dt": ("const double bbar = dt * (double)Bm[t * bc_stride + n];",
+                        "const double bbar = (double)Bm[t * bc_stride + n];"),
+    "B_C_swapped": ("const double bbar = dt * (double)Bm[t * bc_stride + n];",
+                    "const double bbar = dt * (double)Cm[t * bc_stride + n];"),
+    "readout_before_update": (
+        "h[n] = abar * h[n] + bbar * u;\n      acc += (double)Cm[t * bc_stride + n] * h[n];",
+        "acc += (double)Cm[t * bc_stride + n] * h[n];\n      h[n] = abar * h[n] + bbar * u;"),
+    "decay_on_input": ("h[n] = abar * h[n] + bbar * u;", "h[n] = h[n] + abar * bbar * u;"),
+    "conv_taps_reversed": ("u += (double)conv_w[k] * win[k];",
+                           "u += (double)conv_w[K - 2 - k] * win[k];"),
+    "conv_bias_dropped": ("double u = conv_b;", "double u = 0.0 * conv_b;"),
+    "cache_newest_first": ("if (K > 1) win[K - 2] = xt;", "if (K > 1) win[0] = xt;"),
+    "softplus_no_linear_part": ("double pos = v > 0.0 ? v : 0.0;", "double pos = 0.0;"),
+    "softplus_sign": ("return pos + log1p(exp(-fabs(v)));", "return pos + log1p(exp(fabs(v)));"),
+    "dt_bias_subtracted": ("softplus((double)dt_raw[t * act_stride] + dt_bias)",
+                           "softplus((double)dt_raw[t * act_stride] - dt_bias)"),
+    "no_upper_clip": ("if (dt > dt_max) dt = dt_max;", ""),
+    "no_lower_clip": ("if (dt < dt_min) dt = dt_min;", ""),
+    "gate_sigmoid_not_silu": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
+    "D_times_x_not_u": ("acc += D * u;", "acc += D * xt;"),
+    "state_in_ignored": ("h[n] = h_in ? h_in[n] : 0.0;", "h[n] = 0.0;"),
+}
+
+
+def _build_variant(name, old, new, tmpdir):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation {name}: pattern must occur exactly once"
+    path_c = os.path.join(tmpdir, f"{name}.c")
+    with open(path_c, "w") as f:
+        f.write(src.replace(old, new))
+    path_so = os.path.join(tmpdir, f"lib{name}.so")
+    inc = os.path.dirname(SRC)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-I", inc,
+                    "-o", path_so, path_c, "-lm", "-lpthread"], check=True)
+    return oracle.load_library(path_so)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name):
+    old, new = MUTATIONS[name]
+    with tempfile.TemporaryDirectory() as tmpdir:
+        lib = _build_variant(name, old, new, tmpdir)
+        caught = []
+        for pin in oracle_pins.ALL_PINS:
+            try:
+                pin(lib=lib)
+            except (AssertionError, ValueError, FloatingPointError) as exc:  # noqa: PERF203
+                caught.append(pin.__name__)
+                del exc
+        assert caught, f"no pin caught the planted mistake {name}"
