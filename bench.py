@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Benchmark of the Axon-SSM selective-scan prefill on one MI355X.
+
+One step = one call of axon_ssm_prefill over one batch of synthetic input (every step of the hot
+path: conv, dt, scan, readout, gate, cache/state outputs). The default workload is the Axon-SSM
+layer shape the metric is quoted on: batch 1, L = 2048, E = 7680, N = 16, K = 4, fp32.
+Inputs are resident in HBM before timing starts; several input sets are rotated so that each step
+reads data that is not left in the 256 MB last-level (Infinity) cache by the previous step.
+
+Prints one JSON line (rank 0). Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "selective-scan tokens/s at E=7680,N=16,L=2048 + % of HBM peak GB/s"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
+N_STATE, K_CONV = 16, 4
+
+
+def algorithmic_bytes(Bsz, L, E, elt, with_cache_in=False, with_state_in=False):
+    """Bytes the method itself must move for one prefill: x, z, dt_raw, B, C read once, y written
+    once, parameters read once, final state and conv cache written (and read when given)."""
+    act = 3 * Bsz * L * E * elt + 2 * Bsz * L * N_STATE * elt + Bsz * L * E * elt
+    prm = 4 * (E * N_STATE + 3 * E + E * K_CONV)
+    out = 4 * (Bsz * E * N_STATE + Bsz * (K_CONV - 1) * E)
+    inn = (4 * Bsz * (K_CONV - 1) * E if with_cache_in else 0) + \
+        (4 * Bsz * E * N_STATE if with_state_in else 0)
+    return act + prm + out + inn
+
+
+def cpu_baseline(inp, min_seconds=10.0):
+    """The oracle as it is (test infrastructure), timed on the host cores over whole passes of the
+    same workload until min_seconds have elapsed."""
+    import oracle
+
+    threads = min(16, os.cpu_count() or 1)
+    Bsz, L, E = inp["x"].shape
+    oracle.prefill({k: (v[:, :8] if k in ("x", "z", "dt_raw", "B", "C") else v)
+                    for k, v in inp.items()}, threads=threads)  # load / warm up
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.prefill(inp, threads=threads)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": passes * Bsz * L / el, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"whole workload ({Bsz}x{L}x{E}), {passes} passes in {el:.1f} s, "
+                      f"{threads} threads over channels, double precision"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="axon_prefill_f32_b1_l2048_e7680")
+    ap.add_argument("--rotate", type=int, default=3, help="input sets cycled through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM bytes per launch (from rocprofv3 counters), if present")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every (b, e) channel "
+              "is independent, so the path shards over batch and channels with no exchange; run "
+              "one process per GPU on its own share.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import selective_state_space_depthwise_amd as axon
+
+    w = workloads.workload(args.workload)
+    if w.kind != "prefill":
+        sys.exit("bench.py times prefill workloads")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    adt = torch.bfloat16 if w.act == "bf16" else torch.float32
+    elt = 2 if w.act == "bf16" else 4
+    Bsz, L, E = w.batch, w.seqlen, w.d_inner
+
+    inp0 = workloads.prefill_inputs(w)
+    prm = {k: torch.from_numpy(inp0[k]).to(dev) for k in ("A_log", "D", "dt_bias", "conv_w",
+                                                         "conv_b")}
+    sets = []
+    for r in range(args.rotate):
+        inp = inp0 if r == 0 else workloads.prefill_inputs(w, seed_offset=r)
+        s = {k: torch.from_numpy(inp[k]).to(dev).to(adt) for k in ("x", "z", "dt_raw", "B", "C")}
+        s["y"] = torch.empty_like(s["x"])
+        s["cache"] = torch.empty((Bsz, K_CONV - 1, E), dtype=torch.float32, device=dev)
+        s["state"] = torch.empty((Bsz, E, N_STATE), dtype=torch.float32, device=dev)
+        sets.append(s)
+    ws_bytes = axon.prefill_workspace_bytes(Bsz, L, E, w.act == "bf16")
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        s = sets[i % len(sets)]
+        axon.prefill(s["x"], s["z"], s["dt_raw"], s["B"], s["C"], prm["A_log"], prm["D"],
+                     prm["dt_bias"], prm["conv_w"], prm["conv_b"], dt_min=inp0["dt_min"],
+                     dt_max=inp0["dt_max"], y=s["y"], conv_cache_out=s["cache"],
+                     ssm_state_out=s["state"], workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, bracketed by synchronisation; HIP events on the launch stream
+    # bracket each call (all kernels of one prefill).
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(args.warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = np.array([a.elapsed_time(b) for a, b in ev])
+
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = Bsz * L
+    value = tokens / (ms_per_step / 1e3)
+    alg = algorithmic_bytes(Bsz, L, E, elt)
+    launch_ms = float(ev_ms.mean())
+    achieved = alg / (launch_ms / 1e3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+        entry = tj.get(w.name)
+        if entry and entry.get("kernel_source_sha") == _kernel_source_sha():
+            traffic = entry.get("bytes_per_launch")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.act,
+        "data": "synthetic (seeded normal draws, Axon-SSM init for A_log and dt bias)",
+        "config": {"workload": w.name, "batch": Bsz, "seq_len": L, "d_inner": E,
+                   "d_state": N_STATE, "d_conv": K_CONV, "act_dtype": w.act,
+                   "input_sets_rotated": args.rotate},
+        "hbm_gbps": round(achieved, 1),
+        "pct_hbm_peak": round(100.0 * achieved / HBM_PEAK_GBPS, 2),
+        "event_ms": {"mean": round(launch_ms, 5), "min": round(float(ev_ms.min()), 5),
+                     "median": round(float(np.median(ev_ms)), 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": alg},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp0)
+    print(json.dumps(line), flush=True)
+
+
+def _kernel_source_sha():
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "selective_state_space_depthwise_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

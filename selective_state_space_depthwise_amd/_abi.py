@@ -1,0 +1,120 @@
+"""ctypes view of libaxonscan's C ABI (include/axonscan.h). No torch here: pointers are ints.
+
+The library is loaded from this package directory; it is built by
+``python -m selective_state_space_depthwise_amd.build``. There is no fallback: if the library is
+missing or does not load, every entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libaxonscan.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "axonscan.h")
+
+AXON_OK = 0
+AXON_ERR_INVALID_ARGUMENT = 1
+AXON_ERR_UNSUPPORTED = 2
+AXON_ERR_WORKSPACE_TOO_SMALL = 3
+AXON_ERR_HIP = 4
+AXON_F32 = 0
+AXON_BF16 = 1
+
+
+class AxonError(RuntimeError):
+    """A libaxonscan call returned a status other than AXON_OK."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("d_inner", ctypes.c_int64), ("d_state", ctypes.c_int64),
+                ("d_conv", ctypes.c_int64), ("act_dtype", ctypes.c_int)]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("A_log", ctypes.c_void_p), ("D", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+                ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p),
+                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load():
+    """Load libaxonscan.so (once). Raises RuntimeError with a build hint when it is missing."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"libaxonscan.so not found at {LIB_PATH}; build it with "
+                "`python -m selective_state_space_depthwise_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        lib.axon_version.restype = ctypes.c_int
+        lib.axon_version.argtypes = []
+        lib.axon_status_string.restype = ctypes.c_char_p
+        lib.axon_status_string.argtypes = [ctypes.c_int]
+        lib.axon_ssm_prefill_workspace_bytes.restype = ctypes.c_size_t
+        lib.axon_ssm_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Shape)]
+        lib.axon_ssm_prefill.restype = ctypes.c_int
+        lib.axon_ssm_prefill.argtypes = [
+            ctypes.POINTER(Shape), ctypes.POINTER(Params), P, P, P, P, P, P, P, P, P, P, P,
+            ctypes.c_size_t, P]
+        lib.axon_ssm_decode_step.restype = ctypes.c_int
+        lib.axon_ssm_decode_step.argtypes = [
+            ctypes.POINTER(Shape), ctypes.POINTER(Params), P, P, P, P, P, P, P, P, P]
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load().axon_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return load().axon_version()
+
+
+def make_shape(batch, seqlen, d_inner, act_bf16, d_state=16, d_conv=4) -> Shape:
+    return Shape(int(batch), int(seqlen), int(d_inner), int(d_state), int(d_conv),
+                 AXON_BF16 if act_bf16 else AXON_F32)
+
+
+def make_params(A_log, D, dt_bias, conv_w, conv_b, dt_min, dt_max) -> Params:
+    return Params(A_log, D, dt_bias, conv_w, conv_b, float(dt_min), float(dt_max))
+
+
+def workspace_bytes(shape: Shape) -> int:
+    return int(load().axon_ssm_prefill_workspace_bytes(ctypes.byref(shape)))
+
+
+def raw_prefill(shape: Shape, params: Params, x, z, dt_raw, B, C, cache_in, state_in, y,
+                cache_out, state_out, workspace, workspace_bytes_, stream) -> int:
+    """axon_ssm_prefill with integer pointers (0 / None = NULL). Returns the status code."""
+    return load().axon_ssm_prefill(ctypes.byref(shape), ctypes.byref(params), x, z, dt_raw, B, C,
+                                   cache_in, state_in, y, cache_out, state_out, workspace,
+                                   int(workspace_bytes_), stream)
+
+
+def raw_decode_step(shape: Shape, params: Params, x, z, dt_raw, B, C, cache, state, y,
+                    stream) -> int:
+    """axon_ssm_decode_step with integer pointers. Returns the status code."""
+    return load().axon_ssm_decode_step(ctypes.byref(shape), ctypes.byref(params), x, z, dt_raw,
+                                       B, C, cache, state, y, stream)
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/axonscan.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(axon_[a-z0-9_]+)\s*\(", text)))

@@ -1,0 +1,140 @@
+"""Torch-tensor front end of libaxonscan: argument marshalling only.
+
+Every step of the layer runs in the library's HIP kernels. PyTorch supplies device memory (the
+output, cache and workspace tensors allocated here) and the stream (torch's current stream unless
+one is given). Nothing is computed in Python and there is no CPU path.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _abi
+from ._abi import AxonError
+
+D_STATE = 16
+D_CONV = 4
+
+
+def _stream_handle(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def _act_dtype(x: torch.Tensor) -> bool:
+    if x.dtype == torch.float32:
+        return False
+    if x.dtype == torch.bfloat16:
+        return True
+    raise TypeError(f"activations must be float32 or bfloat16, got {x.dtype}")
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _params(A_log, D, dt_bias, conv_w, conv_b, dt_min, dt_max, E, device):
+    for t, n, shp in ((A_log, "A_log", (E, D_STATE)), (D, "D", (E,)), (dt_bias, "dt_bias", (E,)),
+                      (conv_w, "conv_w", (E, D_CONV)), (conv_b, "conv_b", (E,))):
+        _check(t, n, shp, torch.float32, device)
+    return _abi.make_params(A_log.data_ptr(), D.data_ptr(), dt_bias.data_ptr(),
+                            conv_w.data_ptr(), conv_b.data_ptr(), dt_min, dt_max)
+
+
+def prefill_workspace_bytes(batch: int, seqlen: int, d_inner: int, bf16: bool = False) -> int:
+    """Device workspace bytes axon_ssm_prefill needs for this shape."""
+    return _abi.workspace_bytes(_abi.make_shape(batch, seqlen, d_inner, bf16))
+
+
+def prefill(x, z, dt_raw, B, C, A_log, D, dt_bias, conv_w, conv_b, *, dt_min=1e-4, dt_max=100.0,
+            conv_cache_in=None, ssm_state_in=None, y=None, conv_cache_out=None,
+            ssm_state_out=None, workspace=None, stream=None):
+    """Run the layer over x, z, dt_raw (B, L, E) and B, C (B, L, N) on the GPU.
+
+    Activations are float32 or bfloat16 (all the same dtype); parameters float32. Optional
+    ``conv_cache_in`` (B, K-1, E) and ``ssm_state_in`` (B, E, N) are float32 (None = zeros).
+    Outputs may be given (``y``, ``conv_cache_out``, ``ssm_state_out``; the caches may be the
+    inputs themselves for an in-place update) or are allocated. Returns (y, conv_cache, ssm_state).
+    Asynchronous on ``stream`` (default: torch's current stream on x's device)."""
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError("prefill runs on the GPU only; x is on " + str(device))
+    bf16 = _act_dtype(x)
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, seqlen, d_inner)")
+    Bsz, L, E = x.shape
+    for t, n in ((x, "x"), (z, "z"), (dt_raw, "dt_raw")):
+        _check(t, n, (Bsz, L, E), x.dtype, device)
+    for t, n in ((B, "B"), (C, "C")):
+        _check(t, n, (Bsz, L, D_STATE), x.dtype, device)
+    prm = _params(A_log, D, dt_bias, conv_w, conv_b, dt_min, dt_max, E, device)
+    cache_shape, state_shape = (Bsz, D_CONV - 1, E), (Bsz, E, D_STATE)
+    if conv_cache_in is not None:
+        _check(conv_cache_in, "conv_cache_in", cache_shape, torch.float32, device)
+    if ssm_state_in is not None:
+        _check(ssm_state_in, "ssm_state_in", state_shape, torch.float32, device)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", (Bsz, L, E), x.dtype, device)
+    if conv_cache_out is None:
+        conv_cache_out = torch.empty(cache_shape, dtype=torch.float32, device=device)
+    if ssm_state_out is None:
+        ssm_state_out = torch.empty(state_shape, dtype=torch.float32, device=device)
+    _check(conv_cache_out, "conv_cache_out", cache_shape, torch.float32, device)
+    _check(ssm_state_out, "ssm_state_out", state_shape, torch.float32, device)
+    shape = _abi.make_shape(Bsz, L, E, bf16)
+    need = _abi.workspace_bytes(shape)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _abi.raw_prefill(
+        shape, prm, x.data_ptr(), z.data_ptr(), dt_raw.data_ptr(), B.data_ptr(), C.data_ptr(),
+        conv_cache_in.data_ptr() if conv_cache_in is not None else None,
+        ssm_state_in.data_ptr() if ssm_state_in is not None else None,
+        y.data_ptr(), conv_cache_out.data_ptr(), ssm_state_out.data_ptr(), ws_ptr, ws_bytes,
+        _stream_handle(device, stream))
+    if st != _abi.AXON_OK:
+        raise AxonError(st, "axon_ssm_prefill")
+    return y, conv_cache_out, ssm_state_out
+
+
+def decode_step(x, z, dt_raw, B, C, A_log, D, dt_bias, conv_w, conv_b, conv_cache, ssm_state, *,
+                dt_min=1e-4, dt_max=100.0, y=None, stream=None):
+    """One token per batch row: x, z, dt_raw (B, E), B, C (B, N); conv_cache (B, K-1, E) and
+    ssm_state (B, E, N) float32 are updated in place. Returns y (B, E)."""
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError("decode_step runs on the GPU only; x is on " + str(device))
+    bf16 = _act_dtype(x)
+    if x.dim() != 2:
+        raise ValueError("x must be (batch, d_inner)")
+    Bsz, E = x.shape
+    for t, n in ((x, "x"), (z, "z"), (dt_raw, "dt_raw")):
+        _check(t, n, (Bsz, E), x.dtype, device)
+    for t, n in ((B, "B"), (C, "C")):
+        _check(t, n, (Bsz, D_STATE), x.dtype, device)
+    prm = _params(A_log, D, dt_bias, conv_w, conv_b, dt_min, dt_max, E, device)
+    _check(conv_cache, "conv_cache", (Bsz, D_CONV - 1, E), torch.float32, device)
+    _check(ssm_state, "ssm_state", (Bsz, E, D_STATE), torch.float32, device)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", (Bsz, E), x.dtype, device)
+    st = _abi.raw_decode_step(
+        _abi.make_shape(Bsz, 1, E, bf16), prm, x.data_ptr(), z.data_ptr(), dt_raw.data_ptr(),
+        B.data_ptr(), C.data_ptr(), conv_cache.data_ptr(), ssm_state.data_ptr(), y.data_ptr(),
+        _stream_handle(device, stream))
+    if st != _abi.AXON_OK:
+        raise AxonError(st, "axon_ssm_decode_step")
+    return y
+
+
+__all__ = ["prefill", "decode_step", "prefill_workspace_bytes", "AxonError"]

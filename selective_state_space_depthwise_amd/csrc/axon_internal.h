@@ -1,0 +1,58 @@
+// Internal interface between the C-ABI layer (axonscan_api.cpp, plain host C++) and the HIP
+// launchers (axon_kernels.hip). Deliberately free of HIP headers: streams travel as void* and
+// launch results as the integer value of hipError_t (0 = success).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace axon {
+
+constexpr int kState = 16;  // N, states per channel (the Axon-SSM layer configuration)
+constexpr int kConv = 4;    // K, causal conv taps
+constexpr int kHalo = kConv - 1;
+
+// How a prefill is split over time. Chunks are processed in parallel: a first pass scans every
+// chunk but the last from a zero state and keeps its carry (sum of dt, local final state); a
+// small combine pass turns the carries into each chunk's true initial state; the final pass
+// re-scans each chunk from that state and writes the outputs.
+struct PrefillPlan {
+  int64_t chunks = 1;     // M
+  int64_t chunk_len = 0;  // T (tokens per chunk; the last chunk may be shorter)
+  // Workspace regions (byte offsets, 256-byte aligned), used only when chunks > 1.
+  size_t off_carry_h = 0;   // (M, B, E, N) fp32: local final state of each chunk from h = 0
+  size_t off_carry_s = 0;   // (M, B, E) fp32: sum of dt over each chunk
+  size_t off_carry_in = 0;  // (M, B, E, N) fp32: true initial state of each chunk
+  size_t off_halo = 0;      // (B, K-1, E) fp32: copy of conv_cache_in for chunk 0
+  size_t workspace_bytes = 0;
+};
+
+// A pure function of the shape (no device query), so the workspace size is known up front.
+PrefillPlan plan_prefill(int64_t batch, int64_t seqlen, int64_t d_inner);
+
+struct PrefillLaunch {
+  int64_t batch, seqlen, d_inner;
+  int act_bf16;  // 0 = fp32 activations, 1 = bf16
+  const void *x, *z, *dt_raw, *B, *C;
+  const float *A_log, *D, *dt_bias, *conv_w, *conv_b;
+  float dt_min, dt_max;
+  const float *conv_cache_in, *ssm_state_in;  // may be null (zeros)
+  void* y;
+  float *conv_cache_out, *ssm_state_out;
+  void* workspace;
+};
+
+struct DecodeLaunch {
+  int64_t batch, d_inner;
+  int act_bf16;
+  const void *x, *z, *dt_raw, *B, *C;
+  const float *A_log, *D, *dt_bias, *conv_w, *conv_b;
+  float dt_min, dt_max;
+  float *conv_cache, *ssm_state;
+  void* y;
+};
+
+int launch_prefill(const PrefillLaunch& a, const PrefillPlan& plan, void* stream);
+int launch_decode(const DecodeLaunch& a, void* stream);
+
+}  // namespace axon

@@ -1,0 +1,285 @@
+// C ABI of libaxonscan: argument checks, planning, dispatch. Plain host C++ (no HIP headers):
+// every check runs before anything is launched, so an error return leaves device memory and the
+// stream untouched. Semantics of the entry points are documented in include/axonscan.h.
+#include "axonscan.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "axon_internal.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int64_t kMaxBatch = 65535;      // launch grid y dimension
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+// Below this many channel lanes the prefill cuts the sequence into chunks: 256 CUs x 4 SIMDs x
+// 2 waves of 64 lanes.
+constexpr int64_t kTargetLanes = 131072;
+constexpr int64_t kMinChunk = 64;
+constexpr int64_t kMaxChunks = 64;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+};
+
+Span span(const void* p, size_t bytes) {
+  Span s;
+  if (p && bytes) {
+    s.lo = reinterpret_cast<uintptr_t>(p);
+    s.hi = s.lo + bytes;
+  }
+  return s;
+}
+
+bool overlaps(const Span& a, const Span& b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  return !__builtin_mul_overflow(a, b, out) && *out <= kMaxElems;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+axon_status check_shape(const axon_ssm_shape* s, bool prefill) {
+  if (!s) return AXON_ERR_INVALID_ARGUMENT;
+  if (s->d_state != axon::kState || s->d_conv != axon::kConv) return AXON_ERR_UNSUPPORTED;
+  if (s->act_dtype != AXON_F32 && s->act_dtype != AXON_BF16) return AXON_ERR_UNSUPPORTED;
+  if (s->batch < 1 || s->d_inner < 1 || (prefill && s->seqlen < 0))
+    return AXON_ERR_INVALID_ARGUMENT;
+  if (s->batch > kMaxBatch) return AXON_ERR_UNSUPPORTED;
+  int64_t t = 0;
+  const int64_t L = prefill ? s->seqlen : 1;
+  if (!mul_ok(s->batch, L, &t) || !mul_ok(t, s->d_inner, &t) || !mul_ok(t, axon::kState, &t))
+    return AXON_ERR_INVALID_ARGUMENT;
+  if (!mul_ok(s->batch, s->d_inner, &t) || !mul_ok(t, axon::kState, &t))
+    return AXON_ERR_INVALID_ARGUMENT;
+  return AXON_OK;
+}
+
+axon_status check_params(const axon_ssm_params* p) {
+  if (!p) return AXON_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {p->A_log, p->D, p->dt_bias, p->conv_w, p->conv_b};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return AXON_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(p->dt_min) || !std::isfinite(p->dt_max) || p->dt_min < 0.0f ||
+      p->dt_min > p->dt_max)
+    return AXON_ERR_INVALID_ARGUMENT;
+  return AXON_OK;
+}
+
+// Byte spans of the parameter arrays (read-only inputs).
+void param_spans(const axon_ssm_params* p, int64_t E, Span out[5]) {
+  out[0] = span(p->A_log, sizeof(float) * E * axon::kState);
+  out[1] = span(p->D, sizeof(float) * E);
+  out[2] = span(p->dt_bias, sizeof(float) * E);
+  out[3] = span(p->conv_w, sizeof(float) * E * axon::kConv);
+  out[4] = span(p->conv_b, sizeof(float) * E);
+}
+
+}  // namespace
+
+namespace axon {
+
+PrefillPlan plan_prefill(int64_t batch, int64_t seqlen, int64_t d_inner) {
+  PrefillPlan plan;
+  const int64_t channels = batch * d_inner;
+  int64_t M = (kTargetLanes + channels - 1) / channels;
+  int64_t max_m = seqlen / kMinChunk;
+  if (max_m < 1) max_m = 1;
+  if (M > max_m) M = max_m;
+  if (M > kMaxChunks) M = kMaxChunks;
+  if (M < 1) M = 1;
+  int64_t T = (seqlen + M - 1) / M;
+  T = (T + 15) / 16 * 16;
+  if (T < 1) T = 1;
+  M = (seqlen + T - 1) / T;
+  if (M < 1) M = 1;
+  plan.chunks = M;
+  plan.chunk_len = T;
+  if (M > 1) {
+    const size_t be = static_cast<size_t>(channels);
+    size_t off = 0;
+    plan.off_carry_h = off;
+    off = round_up(off + sizeof(float) * M * be * kState, 256);
+    plan.off_carry_s = off;
+    off = round_up(off + sizeof(float) * M * be, 256);
+    plan.off_carry_in = off;
+    off = round_up(off + sizeof(float) * M * be * kState, 256);
+    plan.off_halo = off;
+    off = round_up(off + sizeof(float) * be * kHalo, 256);
+    plan.workspace_bytes = off;
+  }
+  return plan;
+}
+
+}  // namespace axon
+
+extern "C" {
+
+int axon_version(void) { return kVersion; }
+
+const char* axon_status_string(axon_status status) {
+  switch (status) {
+    case AXON_OK: return "ok";
+    case AXON_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case AXON_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case AXON_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case AXON_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+size_t axon_ssm_prefill_workspace_bytes(const axon_ssm_shape* shape) {
+  if (check_shape(shape, true) != AXON_OK) return 0;
+  return axon::plan_prefill(shape->batch, shape->seqlen, shape->d_inner).workspace_bytes;
+}
+
+axon_status axon_ssm_prefill(const axon_ssm_shape* shape, const axon_ssm_params* params,
+                             const void* x, const void* z, const void* dt_raw, const void* B,
+                             const void* C, const float* conv_cache_in,
+                             const float* ssm_state_in, void* y, float* conv_cache_out,
+                             float* ssm_state_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  axon_status st = check_shape(shape, true);
+  if (st != AXON_OK) return st;
+  st = check_params(params);
+  if (st != AXON_OK) return st;
+  const int64_t Bsz = shape->batch, L = shape->seqlen, E = shape->d_inner;
+  const size_t elt = shape->act_dtype == AXON_BF16 ? 2 : 4;
+
+  if (L > 0) {
+    const void* acts[] = {x, z, dt_raw, B, C, y};
+    for (const void* q : acts)
+      if (!q || !aligned16(q)) return AXON_ERR_INVALID_ARGUMENT;
+  }
+  if (!conv_cache_out || !ssm_state_out || !aligned16(conv_cache_out) ||
+      !aligned16(ssm_state_out))
+    return AXON_ERR_INVALID_ARGUMENT;
+  if ((conv_cache_in && !aligned16(conv_cache_in)) || (ssm_state_in && !aligned16(ssm_state_in)))
+    return AXON_ERR_INVALID_ARGUMENT;
+
+  const axon::PrefillPlan plan = axon::plan_prefill(Bsz, L, E);
+  const bool needs_ws = L > 0 && plan.workspace_bytes > 0;
+  if (needs_ws) {
+    if (workspace_bytes < plan.workspace_bytes) return AXON_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace || !aligned16(workspace)) return AXON_ERR_INVALID_ARGUMENT;
+  }
+
+  const size_t act_bytes = elt * Bsz * L * E;
+  const size_t bc_bytes = elt * Bsz * L * axon::kState;
+  const size_t cache_bytes = sizeof(float) * Bsz * axon::kHalo * E;
+  const size_t state_bytes = sizeof(float) * Bsz * E * axon::kState;
+  Span in_x = span(x, act_bytes), in_z = span(z, act_bytes), in_dt = span(dt_raw, act_bytes);
+  Span in_b = span(B, bc_bytes), in_c = span(C, bc_bytes);
+  Span in_cache = span(conv_cache_in, cache_bytes), in_state = span(ssm_state_in, state_bytes);
+  Span out_y = span(y, act_bytes), out_cache = span(conv_cache_out, cache_bytes);
+  Span out_state = span(ssm_state_out, state_bytes);
+  Span ws = needs_ws ? span(workspace, plan.workspace_bytes) : Span{};
+  Span prm[5];
+  param_spans(params, E, prm);
+
+  // y overlaps nothing.
+  const Span others_of_y[] = {in_x, in_z, in_dt, in_b, in_c, in_cache, in_state,
+                              out_cache, out_state, ws, prm[0], prm[1], prm[2], prm[3], prm[4]};
+  for (const Span& o : others_of_y)
+    if (overlaps(out_y, o)) return AXON_ERR_INVALID_ARGUMENT;
+  // cache_out is cache_in (in place) or disjoint from it, and disjoint from everything else.
+  if (conv_cache_in != conv_cache_out && overlaps(out_cache, in_cache))
+    return AXON_ERR_INVALID_ARGUMENT;
+  if (ssm_state_in != ssm_state_out && overlaps(out_state, in_state))
+    return AXON_ERR_INVALID_ARGUMENT;
+  const Span reads[] = {in_x, in_z, in_dt, in_b, in_c, prm[0], prm[1], prm[2], prm[3], prm[4]};
+  for (const Span& r : reads) {
+    if (overlaps(out_cache, r) || overlaps(out_state, r) || overlaps(ws, r))
+      return AXON_ERR_INVALID_ARGUMENT;
+  }
+  if (overlaps(out_cache, out_state) || overlaps(out_cache, in_state) ||
+      overlaps(out_state, in_cache))
+    return AXON_ERR_INVALID_ARGUMENT;
+  const Span rw[] = {in_cache, in_state, out_cache, out_state};
+  for (const Span& r : rw)
+    if (overlaps(ws, r)) return AXON_ERR_INVALID_ARGUMENT;
+
+  axon::PrefillLaunch a{};
+  a.batch = Bsz;
+  a.seqlen = L;
+  a.d_inner = E;
+  a.act_bf16 = shape->act_dtype == AXON_BF16;
+  a.x = x;
+  a.z = z;
+  a.dt_raw = dt_raw;
+  a.B = B;
+  a.C = C;
+  a.A_log = params->A_log;
+  a.D = params->D;
+  a.dt_bias = params->dt_bias;
+  a.conv_w = params->conv_w;
+  a.conv_b = params->conv_b;
+  a.dt_min = params->dt_min;
+  a.dt_max = params->dt_max;
+  a.conv_cache_in = conv_cache_in;
+  a.ssm_state_in = ssm_state_in;
+  a.y = y;
+  a.conv_cache_out = conv_cache_out;
+  a.ssm_state_out = ssm_state_out;
+  a.workspace = needs_ws ? workspace : nullptr;
+  return axon::launch_prefill(a, plan, stream) == 0 ? AXON_OK : AXON_ERR_HIP;
+}
+
+axon_status axon_ssm_decode_step(const axon_ssm_shape* shape, const axon_ssm_params* params,
+                                 const void* x, const void* z, const void* dt_raw, const void* B,
+                                 const void* C, float* conv_cache, float* ssm_state, void* y,
+                                 void* stream) {
+  axon_status st = check_shape(shape, false);
+  if (st != AXON_OK) return st;
+  st = check_params(params);
+  if (st != AXON_OK) return st;
+  const void* ptrs[] = {x, z, dt_raw, B, C, conv_cache, ssm_state, y};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return AXON_ERR_INVALID_ARGUMENT;
+  const int64_t Bsz = shape->batch, E = shape->d_inner;
+  const size_t elt = shape->act_dtype == AXON_BF16 ? 2 : 4;
+  Span in_x = span(x, elt * Bsz * E), in_z = span(z, elt * Bsz * E);
+  Span in_dt = span(dt_raw, elt * Bsz * E);
+  Span in_b = span(B, elt * Bsz * axon::kState), in_c = span(C, elt * Bsz * axon::kState);
+  Span cache = span(conv_cache, sizeof(float) * Bsz * axon::kHalo * E);
+  Span state = span(ssm_state, sizeof(float) * Bsz * E * axon::kState);
+  Span out_y = span(y, elt * Bsz * E);
+  Span prm[5];
+  param_spans(params, E, prm);
+  const Span reads[] = {in_x, in_z, in_dt, in_b, in_c, prm[0], prm[1], prm[2], prm[3], prm[4]};
+  for (const Span& r : reads) {
+    if (overlaps(out_y, r) || overlaps(cache, r) || overlaps(state, r))
+      return AXON_ERR_INVALID_ARGUMENT;
+  }
+  if (overlaps(out_y, cache) || overlaps(out_y, state) || overlaps(cache, state))
+    return AXON_ERR_INVALID_ARGUMENT;
+
+  axon::DecodeLaunch a{};
+  a.batch = Bsz;
+  a.d_inner = E;
+  a.act_bf16 = shape->act_dtype == AXON_BF16;
+  a.x = x;
+  a.z = z;
+  a.dt_raw = dt_raw;
+  a.B = B;
+  a.C = C;
+  a.A_log = params->A_log;
+  a.D = params->D;
+  a.dt_bias = params->dt_bias;
+  a.conv_w = params->conv_w;
+  a.conv_b = params->conv_b;
+  a.dt_min = params->dt_min;
+  a.dt_max = params->dt_max;
+  a.conv_cache = conv_cache;
+  a.ssm_state = ssm_state;
+  a.y = y;
+  return axon::launch_decode(a, stream) == 0 ? AXON_OK : AXON_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, run the HIP path through
+the binding, and compare with the oracle element by element.
+
+Tolerances (element-wise, against the oracle run on the same rounded inputs):
+  fp32 activations: |gpu - ref| <= 1e-4 * (1 + |ref|)
+  bf16 activations: |gpu - ref| <= 2e-2 * (1 + |ref|)   (y is rounded to bf16; state stays fp32)
+  conv cache: bit-exact (it holds copies of the inputs).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+# The state is fp32 in both cases; for bf16 runs its error is set by the same fp32 arithmetic.
+STATE_TOL = {"f32": 1e-4, "bf16": 1e-4}
+ACT_KEYS = ("x", "z", "dt_raw", "B", "C")
+PARAM_KEYS = ("A_log", "D", "dt_bias", "conv_w", "conv_b")
+
+
+def say(msg: str) -> None:
+    """Print and flush a line naming the case, so a failure can be located from the log."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def device():
+    return torch.device("cuda:0")
+
+
+def act_dtype(act: str):
+    return torch.bfloat16 if act == "bf16" else torch.float32
+
+
+def to_device(inp: dict, act: str | None = None) -> dict:
+    act = act or inp.get("act", "f32")
+    dev = device()
+    out = {}
+    for k in ACT_KEYS:
+        out[k] = torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev).to(act_dtype(act))
+    for k in PARAM_KEYS:
+        out[k] = torch.from_numpy(np.ascontiguousarray(inp[k], np.float32)).to(dev)
+    out["dt_min"], out["dt_max"] = float(inp["dt_min"]), float(inp["dt_max"])
+    return out
+
+
+def gpu_prefill(d: dict, **kw):
+    import selective_state_space_depthwise_amd as axon
+
+    return axon.prefill(d["x"], d["z"], d["dt_raw"], d["B"], d["C"], d["A_log"], d["D"],
+                        d["dt_bias"], d["conv_w"], d["conv_b"], dt_min=d["dt_min"],
+                        dt_max=d["dt_max"], **kw)
+
+
+def gpu_decode(step: dict, d: dict, cache, state, **kw):
+    import selective_state_space_depthwise_amd as axon
+
+    return axon.decode_step(step["x"], step["z"], step["dt_raw"], step["B"], step["C"],
+                            d["A_log"], d["D"], d["dt_bias"], d["conv_w"], d["conv_b"], cache,
+                            state, dt_min=d["dt_min"], dt_max=d["dt_max"], **kw)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str) -> None:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite values from the GPU"
+    err = np.abs(got - ref)
+    bound = tol * (1.0 + np.abs(ref))
+    bad = err > bound
+    if bad.any():
+        idx = np.unravel_index(np.argmax(err / bound), err.shape)
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {bad.size} elements beyond {tol}*(1+|ref|); worst at "
+            f"{idx}: gpu={got[idx]!r} ref={ref[idx]!r} err={err[idx]:.3e}")
+
+
+def max_rel(got, ref) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.max(np.abs(got - ref) / (1.0 + np.abs(ref)))) if got.size else 0.0
+
+
+def sample_channels(Bsz: int, E: int, n: int, seed: int = 0):
+    """Channel (b, e) pairs to check at full size: the corners, wave boundaries, random others."""
+    g = np.random.default_rng(seed)
+    picks = {(0, 0), (Bsz - 1, E - 1), (0, E - 1), (Bsz - 1, 0)}
+    for e in (63, 64, 65, E // 2):
+        if e < E:
+            picks.add((int(g.integers(Bsz)), e))
+    while len(picks) < n:
+        picks.add((int(g.integers(Bsz)), int(g.integers(E))))
+    return sorted(picks)
+
+
+def single_channel_inputs(params: dict, e: int, seq: dict) -> dict:
+    """A (1, L, 1) case for the oracle made of channel e's parameters and per-token sequences
+    x, z, dt_raw (L,) and B, C (L, N)."""
+    L = len(seq["x"])
+    return {
+        "x": np.asarray(seq["x"], np.float32).reshape(1, L, 1),
+        "z": np.asarray(seq["z"], np.float32).reshape(1, L, 1),
+        "dt_raw": np.asarray(seq["dt_raw"], np.float32).reshape(1, L, 1),
+        "B": np.asarray(seq["B"], np.float32).reshape(1, L, -1),
+        "C": np.asarray(seq["C"], np.float32).reshape(1, L, -1),
+        "A_log": params["A_log"][e:e + 1], "D": params["D"][e:e + 1],
+        "dt_bias": params["dt_bias"][e:e + 1], "conv_w": params["conv_w"][e:e + 1],
+        "conv_b": params["conv_b"][e:e + 1], "dt_min": params["dt_min"],
+        "dt_max": params["dt_max"],
+    }

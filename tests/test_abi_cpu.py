@@ -1,0 +1,169 @@
+"""libaxonscan's C ABI on the CPU: the library loads, exports what the header declares, sizes its
+workspace from the shape alone, and rejects bad arguments before anything is launched. No call
+here passes validation, so nothing reaches the GPU (fake pointers are never dereferenced)."""
+import ctypes
+
+import pytest
+
+from selective_state_space_depthwise_amd import _abi
+
+A = _abi
+P = 0x7F0000000000  # a fake, 16-byte aligned device address; never dereferenced
+
+
+def _shape(batch=1, seqlen=64, d_inner=32, bf16=False, d_state=16, d_conv=4):
+    return A.make_shape(batch, seqlen, d_inner, bf16, d_state=d_state, d_conv=d_conv)
+
+
+def _params(dt_min=1e-4, dt_max=100.0, base=P + (1 << 30)):
+    return A.make_params(base, base + (1 << 20), base + (2 << 20), base + (3 << 20),
+                         base + (4 << 20), dt_min, dt_max)
+
+
+def _buffers():
+    """Disjoint fake buffers, 64 MiB apart."""
+    names = ["x", "z", "dt", "B", "C", "cin", "sin", "y", "cout", "sout", "ws"]
+    return {n: P + (i + 1) * (64 << 20) for i, n in enumerate(names)}
+
+
+def _prefill(shape=None, params=None, ws_bytes=1 << 30, **over):
+    b = _buffers()
+    b.update(over)
+    return A.raw_prefill(shape or _shape(), params or _params(), b["x"], b["z"], b["dt"], b["B"],
+                         b["C"], b["cin"], b["sin"], b["y"], b["cout"], b["sout"], b["ws"],
+                         ws_bytes, None)
+
+
+def _decode(shape=None, params=None, **over):
+    b = _buffers()
+    b.update(over)
+    return A.raw_decode_step(shape or _shape(seqlen=1), params or _params(), b["x"], b["z"],
+                             b["dt"], b["B"], b["C"], b["cin"], b["sin"], b["y"], None)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = A.load()
+    declared = A.declared_functions()
+    assert set(declared) >= {"axon_ssm_prefill", "axon_ssm_decode_step",
+                             "axon_ssm_prefill_workspace_bytes", "axon_status_string",
+                             "axon_version"}
+    for name in declared:
+        assert hasattr(lib, name), f"{name} is declared in include/axonscan.h but not exported"
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings():
+    assert A.version() == 100
+    for st in range(5):
+        assert A.status_string(st)
+    assert A.status_string(99) == "unknown status"
+
+
+def test_workspace_is_a_pure_function_of_shape():
+    # enough channels to fill the GPU: no time chunks, no workspace
+    assert A.workspace_bytes(_shape(1, 64, 32)) == 0
+    assert A.workspace_bytes(_shape(64, 1, 7680)) == 0
+    # few channels, long sequence: chunked, workspace = carries + halo
+    ws1 = A.workspace_bytes(_shape(1, 2048, 7680))
+    assert ws1 == A.workspace_bytes(_shape(1, 2048, 7680))
+    assert ws1 > 2 * 16 * 4 * 7680  # at least two chunks of carries
+    assert ws1 % 256 == 0
+    assert A.workspace_bytes(_shape(2, 65536, 2048, True)) > 0
+    # invalid shapes report 0
+    assert A.workspace_bytes(_shape(d_state=8)) == 0
+    assert A.workspace_bytes(_shape(batch=0)) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_state=8), A.AXON_ERR_UNSUPPORTED),
+    (dict(d_state=32), A.AXON_ERR_UNSUPPORTED),
+    (dict(d_conv=3), A.AXON_ERR_UNSUPPORTED),
+    (dict(batch=0), A.AXON_ERR_INVALID_ARGUMENT),
+    (dict(d_inner=0), A.AXON_ERR_INVALID_ARGUMENT),
+    (dict(seqlen=-1), A.AXON_ERR_INVALID_ARGUMENT),
+    (dict(batch=70000), A.AXON_ERR_UNSUPPORTED),
+    (dict(batch=4, seqlen=1 << 30, d_inner=1 << 20), A.AXON_ERR_INVALID_ARGUMENT),
+])
+def test_prefill_rejects_bad_shapes(kw, status):
+    assert _prefill(shape=_shape(**kw)) == status
+
+
+def test_prefill_rejects_unknown_dtype():
+    s = _shape()
+    s.act_dtype = 7
+    assert _prefill(shape=s) == A.AXON_ERR_UNSUPPORTED
+
+
+def test_prefill_rejects_null_shape_and_params():
+    lib = A.load()
+    b = _buffers()
+    st = lib.axon_ssm_prefill(None, ctypes.byref(_params()), b["x"], b["z"], b["dt"], b["B"],
+                              b["C"], None, None, b["y"], b["cout"], b["sout"], b["ws"], 0, None)
+    assert st == A.AXON_ERR_INVALID_ARGUMENT
+    sh = _shape()
+    st = lib.axon_ssm_prefill(ctypes.byref(sh), None, b["x"], b["z"], b["dt"], b["B"], b["C"],
+                              None, None, b["y"], b["cout"], b["sout"], b["ws"], 0, None)
+    assert st == A.AXON_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("name", ["x", "z", "dt", "B", "C", "y", "cout", "sout"])
+def test_prefill_rejects_null_required_pointer(name):
+    assert _prefill(**{name: None}) == A.AXON_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("name", ["x", "z", "dt", "B", "C", "y", "cout", "sout", "cin", "sin"])
+def test_prefill_rejects_misaligned_pointer(name):
+    b = _buffers()
+    assert _prefill(**{name: b[name] + 4}) == A.AXON_ERR_INVALID_ARGUMENT
+
+
+def test_prefill_rejects_bad_params():
+    assert _prefill(params=_params(dt_min=1.0, dt_max=0.5)) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _prefill(params=_params(dt_min=float("nan"))) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _prefill(params=_params(dt_max=float("inf"))) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _prefill(params=_params(dt_min=-1.0)) == A.AXON_ERR_INVALID_ARGUMENT
+    p = _params()
+    p.A_log = None
+    assert _prefill(params=p) == A.AXON_ERR_INVALID_ARGUMENT
+    p = _params()
+    p.conv_w = p.conv_w + 8
+    assert _prefill(params=p) == A.AXON_ERR_INVALID_ARGUMENT
+
+
+def test_prefill_workspace_checks():
+    sh = _shape(1, 2048, 7680)
+    need = A.workspace_bytes(sh)
+    assert need > 0
+    assert _prefill(shape=sh, ws_bytes=need - 1) == A.AXON_ERR_WORKSPACE_TOO_SMALL
+    assert _prefill(shape=sh, ws_bytes=need, ws=None) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _prefill(shape=sh, ws_bytes=need, ws=_buffers()["ws"] + 8) == \
+        A.AXON_ERR_INVALID_ARGUMENT
+
+
+def test_prefill_rejects_forbidden_aliasing():
+    b = _buffers()
+    # y on top of an input
+    assert _prefill(y=b["x"]) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _prefill(y=b["B"] + 16) == A.AXON_ERR_INVALID_ARGUMENT
+    # partial overlap of a cache with its input (exact equality is the allowed in-place form)
+    assert _prefill(cout=b["cin"] + 16) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _prefill(sout=b["sin"] + 16) == A.AXON_ERR_INVALID_ARGUMENT
+    # cache/state outputs over read-only inputs, or over each other
+    assert _prefill(cout=b["x"]) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _prefill(sout=b["cout"]) == A.AXON_ERR_INVALID_ARGUMENT
+    # workspace over an output
+    sh = _shape(1, 2048, 7680)
+    assert _prefill(shape=sh, ws=b["y"]) == A.AXON_ERR_INVALID_ARGUMENT
+
+
+def test_decode_rejects_bad_arguments():
+    assert _decode(shape=_shape(seqlen=1, d_state=4)) == A.AXON_ERR_UNSUPPORTED
+    assert _decode(shape=_shape(seqlen=1, batch=0)) == A.AXON_ERR_INVALID_ARGUMENT
+    for name in ["x", "z", "dt", "B", "C", "cin", "sin", "y"]:
+        assert _decode(**{name: None}) == A.AXON_ERR_INVALID_ARGUMENT
+        assert _decode(**{name: _buffers()[name] + 4}) == A.AXON_ERR_INVALID_ARGUMENT
+    b = _buffers()
+    assert _decode(y=b["x"]) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _decode(y=b["cin"]) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _decode(sin=b["cin"]) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _decode(params=_params(dt_min=2.0, dt_max=1.0)) == A.AXON_ERR_INVALID_ARGUMENT

@@ -74,11 +74,13 @@ def _rng(seed: int, tid: int) -> np.random.Generator:
 
 
 def bf16_round(a: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bfloat16 (ties to even); returned as float32."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    bits = a.view(np.uint32).astype(np.uint64)
-    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000
-    return bits.astype(np.uint32).view(np.float32).reshape(a.shape)
+    """Round float32 values to the nearest bfloat16 (ties to even); returned as float32.
+    (Finite inputs only: the 32-bit sum below cannot overflow for them.)"""
+    out = np.array(a, dtype=np.float32, copy=True, order="C")
+    u = out.view(np.uint32)
+    u += np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    u &= np.uint32(0xFFFF0000)
+    return out
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
