@@ -53,11 +53,11 @@ def _declare(lib):
     Dd = ctypes.c_double
     lib.oracle_ssm_channel.restype = ctypes.c_int
     lib.oracle_ssm_channel.argtypes = [
-        I, I, I, P, P, P, I, P, P, I, P, Dd, Dd, P, Dd, Dd, Dd, P, P, P, I, P, P, P, P,
+        I, I, I, P, P, P, I, P, P, I, P, Dd, Dd, P, Dd, Dd, Dd, P, P, P, I, P, P, P, P, P,
     ]
     lib.oracle_ssm_prefill.restype = ctypes.c_int
     lib.oracle_ssm_prefill.argtypes = [
-        I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, Dd, Dd, P, P, P, P, P, ctypes.c_int,
+        I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, Dd, Dd, P, P, P, P, P, P, ctypes.c_int,
     ]
     lib.oracle_ssm_decode_step.restype = ctypes.c_int
     lib.oracle_ssm_decode_step.argtypes = [
@@ -95,8 +95,10 @@ def _ptr(a):
 
 
 def prefill(inp: dict, conv_cache_in=None, ssm_state_in=None, threads: int = 1,
-            lib=None) -> dict:
-    """Run the oracle over whole (B, L, E) tensors. Returns y, conv_cache, ssm_state (float64)."""
+            lib=None, magnitude: bool = False) -> dict:
+    """Run the oracle over whole (B, L, E) tensors. Returns y, conv_cache, ssm_state (float64),
+    and with ``magnitude`` also ``mag``: |SiLU(z)| * (sum_n |C h_n| + |D u|) per token, the size
+    of the terms each output sums (a conditioning diagnostic)."""
     lib = _load(lib)
     x, z, dtr = _f32(inp["x"]), _f32(inp["z"]), _f32(inp["dt_raw"])
     Bm, Cm = _f32(inp["B"]), _f32(inp["C"])
@@ -115,20 +117,24 @@ def prefill(inp: dict, conv_cache_in=None, ssm_state_in=None, threads: int = 1,
     y = np.empty((Bsz, L, E), np.float64)
     cout = np.empty((Bsz, K - 1, E), np.float64)
     sout = np.empty((Bsz, E, N), np.float64)
+    mag = np.empty((Bsz, L, E), np.float64) if magnitude else None
     rc = lib.oracle_ssm_prefill(
         Bsz, L, E, N, K, _ptr(x), _ptr(z), _ptr(dtr), _ptr(Bm), _ptr(Cm), _ptr(A_log), _ptr(D),
         _ptr(dtb), _ptr(w), _ptr(cb), float(inp["dt_min"]), float(inp["dt_max"]), _ptr(cin),
-        _ptr(sin), _ptr(y), _ptr(cout), _ptr(sout), int(threads),
+        _ptr(sin), _ptr(y), _ptr(cout), _ptr(sout), _ptr(mag), int(threads),
     )
     if rc != 0:
         raise ValueError("oracle_ssm_prefill rejected its arguments")
-    return {"y": y, "conv_cache": cout, "ssm_state": sout}
+    out = {"y": y, "conv_cache": cout, "ssm_state": sout}
+    if magnitude:
+        out["mag"] = mag
+    return out
 
 
 def channel(inp: dict, b: int, e: int, conv_cache_in=None, ssm_state_in=None, lib=None) -> dict:
     """Run the oracle for one (b, e) channel over all L tokens.
 
-    Returns y (L,), u (L,), dt (L,), conv_cache (K-1,), ssm_state (N,) as float64.
+    Returns y (L,), u (L,), dt (L,), mag (L,), conv_cache (K-1,), ssm_state (N,) as float64.
     ``conv_cache_in`` / ``ssm_state_in`` are the whole (B, K-1, E) / (B, E, N) arrays or None.
     """
     lib = _load(lib)
@@ -148,17 +154,18 @@ def channel(inp: dict, b: int, e: int, conv_cache_in=None, ssm_state_in=None, li
     y = np.empty(L, np.float64)
     u = np.empty(L, np.float64)
     dt = np.empty(L, np.float64)
+    mag = np.empty(L, np.float64)
     wout = np.empty(max(K - 1, 1), np.float64)
     hout = np.empty(N, np.float64)
     rc = lib.oracle_ssm_channel(
         L, N, K, _ptr(xc), _ptr(zc), _ptr(dc), 1, _ptr(Bc), _ptr(Cc), N, _ptr(A_log[e]),
         float(inp["D"][e]), float(inp["dt_bias"][e]), _ptr(w[e]), float(inp["conv_b"][e]),
         float(inp["dt_min"]), float(inp["dt_max"]), _ptr(win), _ptr(h0), _ptr(y), 1,
-        _ptr(wout), _ptr(hout), _ptr(u), _ptr(dt),
+        _ptr(wout), _ptr(hout), _ptr(u), _ptr(dt), _ptr(mag),
     )
     if rc != 0:
         raise ValueError("oracle_ssm_channel rejected its arguments")
-    return {"y": y, "u": u, "dt": dt, "conv_cache": wout[: K - 1], "ssm_state": hout}
+    return {"y": y, "u": u, "dt": dt, "mag": mag, "conv_cache": wout[: K - 1], "ssm_state": hout}
 
 
 def decode_step(step: dict, params: dict, conv_cache, ssm_state, threads: int = 1,

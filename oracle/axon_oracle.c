@@ -32,7 +32,7 @@ int oracle_ssm_channel(int64_t L, int64_t N, int64_t K,
                        double conv_b, double dt_min, double dt_max,
                        const double* win_in, const double* h_in,
                        double* y, int64_t y_stride, double* win_out, double* h_out,
-                       double* u_out, double* dt_out) {
+                       double* u_out, double* dt_out, double* mag_out) {
   if (L < 0 || N < 1 || K < 1 || N > 4096 || K > 64) return -1;
   if (L > 0 && (!x || !z || !dt_raw || !Bm || !Cm || !y)) return -1;
   if (!A_log || !conv_w || !win_out || !h_out) return -1;
@@ -75,19 +75,23 @@ int oracle_ssm_channel(int64_t L, int64_t N, int64_t K,
      * h_t = Abar h_{t-1} + Bbar x_t and y_t = C h_t + D x_t, with the convolution output u_t as
      * the scan input x_t in both places. [AXON "ZOH discretization"; WIKI "Selective scan (toy)"]
      * READING: the skip term D uses the same u_t as the recurrence. */
-    double acc = 0.0;
+    double acc = 0.0, mag = 0.0;
     for (int64_t n = 0; n < N; ++n) {
       const double abar = exp(dt * A[n]);
       const double bbar = dt * (double)Bm[t * bc_stride + n];
       h[n] = abar * h[n] + bbar * u;
       acc += (double)Cm[t * bc_stride + n] * h[n];
+      mag += fabs((double)Cm[t * bc_stride + n] * h[n]);
     }
     acc += D * u;
+    mag += fabs(D * u);
 
     /* Gate: y * SiLU(z).  [AXON "Gating"] */
-    y[t * y_stride] = acc * silu((double)z[t * act_stride]);
+    const double gate = silu((double)z[t * act_stride]);
+    y[t * y_stride] = acc * gate;
     if (u_out) u_out[t * y_stride] = u;
     if (dt_out) dt_out[t * y_stride] = dt;
+    if (mag_out) mag_out[t * y_stride] = mag * fabs(gate);
   }
 
   for (int64_t k = 0; k < K - 1; ++k) win_out[k] = win[k];
@@ -105,7 +109,7 @@ typedef struct {
   const float *x, *z, *dt_raw, *Bm, *Cm, *A_log, *D, *dt_bias, *conv_w, *conv_b;
   double dt_min, dt_max;
   const double *cache_in, *state_in;
-  double *y, *cache_out, *state_out;
+  double *y, *cache_out, *state_out, *mag;
   int64_t ch_begin, ch_end; /* channel index c = b * E + e */
   int status;
 } prefill_job;
@@ -131,7 +135,8 @@ static void* prefill_worker(void* arg) {
         has_tokens ? j->dt_raw + off : NULL, E, has_tokens ? j->Bm + b * L * N : NULL,
         has_tokens ? j->Cm + b * L * N : NULL, N, j->A_log + e * N, (double)j->D[e],
         (double)j->dt_bias[e], j->conv_w + e * K, (double)j->conv_b[e], j->dt_min, j->dt_max,
-        win_in, h_in, has_tokens ? j->y + off : NULL, E, win_out, h_out, NULL, NULL);
+        win_in, h_in, has_tokens ? j->y + off : NULL, E, win_out, h_out, NULL, NULL,
+        (has_tokens && j->mag) ? j->mag + off : NULL);
     for (int64_t k = 0; k < K - 1; ++k) j->cache_out[(b * (K - 1) + k) * E + e] = win_out[k];
     for (int64_t n = 0; n < N; ++n) j->state_out[(b * E + e) * N + n] = h_out[n];
   }
@@ -175,7 +180,8 @@ int oracle_ssm_prefill(int64_t Bsz, int64_t L, int64_t E, int64_t N, int64_t K,
                        const float* A_log, const float* D, const float* dt_bias,
                        const float* conv_w, const float* conv_b, double dt_min, double dt_max,
                        const double* conv_cache_in, const double* ssm_state_in,
-                       double* y, double* conv_cache_out, double* ssm_state_out, int threads) {
+                       double* y, double* conv_cache_out, double* ssm_state_out, double* mag,
+                       int threads) {
   if (Bsz < 1 || E < 1 || L < 0 || N < 1 || K < 1 || K > 64) return -1;
   if (!A_log || !D || !dt_bias || !conv_w || !conv_b || !conv_cache_out || !ssm_state_out)
     return -1;
@@ -187,6 +193,7 @@ int oracle_ssm_prefill(int64_t Bsz, int64_t L, int64_t E, int64_t N, int64_t K,
   proto.conv_b = conv_b; proto.dt_min = dt_min; proto.dt_max = dt_max;
   proto.cache_in = conv_cache_in; proto.state_in = ssm_state_in;
   proto.y = y; proto.cache_out = conv_cache_out; proto.state_out = ssm_state_out;
+  proto.mag = mag;
   return run_jobs(&proto, threads);
 }
 
@@ -201,5 +208,5 @@ int oracle_ssm_decode_step(int64_t Bsz, int64_t E, int64_t N, int64_t K,
    * them, so passing the same arrays as input and output is safe. */
   return oracle_ssm_prefill(Bsz, 1, E, N, K, x, z, dt_raw, Bm, Cm, A_log, D, dt_bias, conv_w,
                             conv_b, dt_min, dt_max, conv_cache, ssm_state, y, conv_cache,
-                            ssm_state, threads);
+                            ssm_state, NULL, threads);
 }

@@ -28,6 +28,9 @@ extern "C" {
  *   win_out      : K-1 values, the last K-1 x-branch inputs of [win_in, x], oldest first
  *   h_out        : N final states
  *   u_out, dt_out: optional (may be NULL) per-token conv output and step size, [t * y_stride]
+ *   mag_out      : optional (may be NULL) per-token size of the terms the output sums,
+ *                  |SiLU(z_t)| * (sum_n |C_t,n h_t,n| + |D u_t|), [t * y_stride]; it bounds how
+ *                  much rounding of those terms can move y_t (a diagnostic, not part of y)
  * Returns 0, or -1 for an invalid argument. */
 int oracle_ssm_channel(int64_t L, int64_t N, int64_t K,
                        const float* x, const float* z, const float* dt_raw, int64_t act_stride,
@@ -36,12 +39,13 @@ int oracle_ssm_channel(int64_t L, int64_t N, int64_t K,
                        double conv_b, double dt_min, double dt_max,
                        const double* win_in, const double* h_in,
                        double* y, int64_t y_stride, double* win_out, double* h_out,
-                       double* u_out, double* dt_out);
+                       double* u_out, double* dt_out, double* mag_out);
 
 /* Whole prefill over (B, L, E) tensors laid out as in libaxonscan's header:
  *   x, z, dt_raw (B,L,E); Bm, Cm (B,L,N); A_log (E,N); D, dt_bias, conv_b (E); conv_w (E,K);
  *   conv_cache_in (B,K-1,E) or NULL; ssm_state_in (B,E,N) or NULL;
- *   y (B,L,E); conv_cache_out (B,K-1,E); ssm_state_out (B,E,N).
+ *   y (B,L,E); conv_cache_out (B,K-1,E); ssm_state_out (B,E,N); mag (B,L,E) or NULL (see
+ *   mag_out above).
  * threads >= 1 splits the independent channels over that many POSIX threads. */
 int oracle_ssm_prefill(int64_t Bsz, int64_t L, int64_t E, int64_t N, int64_t K,
                        const float* x, const float* z, const float* dt_raw,
@@ -49,7 +53,8 @@ int oracle_ssm_prefill(int64_t Bsz, int64_t L, int64_t E, int64_t N, int64_t K,
                        const float* A_log, const float* D, const float* dt_bias,
                        const float* conv_w, const float* conv_b, double dt_min, double dt_max,
                        const double* conv_cache_in, const double* ssm_state_in,
-                       double* y, double* conv_cache_out, double* ssm_state_out, int threads);
+                       double* y, double* conv_cache_out, double* ssm_state_out, double* mag,
+                       int threads);
 
 /* One decode step: x, z, dt_raw (B,E); Bm, Cm (B,N); conv_cache (B,K-1,E) and ssm_state (B,E,N)
  * are read and overwritten; y (B,E). */

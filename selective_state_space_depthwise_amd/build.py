@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libaxonscan.so")
 
-HIP_SOURCES = ["axon_kernels.hip"]
+HIP_SOURCES = ["axon_kernels.hip", "axon_rowscan.hip"]
 CXX_SOURCES = ["axonscan_api.cpp"]
 ARCH = "gfx950"
 # Packed-FP32 instructions stay off: the compiler would otherwise form v_pk_* FP32 ops on its own.

@@ -12,11 +12,14 @@ constexpr int kState = 16;  // N, states per channel (the Axon-SSM layer configu
 constexpr int kConv = 4;    // K, causal conv taps
 constexpr int kHalo = kConv - 1;
 
-// How a prefill is split over time. Chunks are processed in parallel: a first pass scans every
-// chunk but the last from a zero state and keeps its carry (sum of dt, local final state); a
-// small combine pass turns the carries into each chunk's true initial state; the final pass
-// re-scans each chunk from that state and writes the outputs.
+// How a prefill is split. The scan kernel spreads each channel's 16 states over 4 * row_waves
+// (lane row, wave) pairs. When even that leaves the GPU short of lanes, the sequence is also cut
+// into chunks processed in parallel: a first pass scans every chunk but the last from a zero
+// state and keeps its carry (sum of dt, local final state); a small combine pass turns the
+// carries into each chunk's true initial state; the final pass re-scans each chunk from that
+// state and writes the outputs.
 struct PrefillPlan {
+  int row_waves = 2;      // W: waves per 16-channel group (states per lane = 4 / W)
   int64_t chunks = 1;     // M
   int64_t chunk_len = 0;  // T (tokens per chunk; the last chunk may be shorter)
   // Workspace regions (byte offsets, 256-byte aligned), used only when chunks > 1.
@@ -53,6 +56,7 @@ struct DecodeLaunch {
 };
 
 int launch_prefill(const PrefillLaunch& a, const PrefillPlan& plan, void* stream);
+int launch_row_scan(const PrefillLaunch& a, const PrefillPlan& plan, void* stream);
 int launch_decode(const DecodeLaunch& a, void* stream);
 
 }  // namespace axon

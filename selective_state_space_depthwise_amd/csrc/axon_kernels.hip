@@ -1,148 +1,18 @@
-// HIP kernels (gfx950) of the Axon-SSM selective-scan hot path and their launchers.
+// HIP kernels (gfx950) besides the prefill scan: the single-token decode step, the carry combine
+// of the time-chunked prefill, the empty-sequence cache copy, and the prefill dispatch.
 //
-// What is computed follows "Axon-SSM: Selective State Space Model for Apple Silicon":
-//   conv:   u_t = conv_b + sum_k w_k x_{t-3+k}                 (section "Key contributions")
-//   dt:     dt_t = clip(softplus(dt_raw_t + dt_bias), lo, hi)  (section "Selective mechanism")
-//   decay:  Abar = exp(dt A) with A = -exp(A_log)              (sections "ZOH discretization",
-//                                                               "Diagonal state matrix")
-//   state:  h_n = Abar_n h_n + dt B_{t,n} u_t;  y_t = C_t . h + D u_t
-//   gate:   out_t = y_t * SiLU(z_t)                            (section "Gating")
-// All arithmetic is fp32; bf16 activations are widened on load and rounded to nearest even on
-// store.
-//
-// Work split. One lane owns one (b, e) channel and keeps its 16 states in VGPRs; a wave covers 64
-// consecutive channels of one batch row, so the B_t / C_t rows it reads are wave-uniform (scalar
-// loads) and the x / z / dt_raw / y rows are contiguous across the wave. When batch*d_inner
-// channels are too few to fill the GPU, the sequence is cut into M chunks and the recurrence is
-// split into three launches (a two-level scan over time):
-//   1. scan_carry:   chunks 0..M-2 scanned from h = 0; keep (S_c = sum dt, h_c).
-//   2. carry_combine: H_0 = state_in; H_{c+1} = exp(A S_c) * H_c + h_c (the product of the
-//      chunk's decays exp(dt A) is exp(A * sum dt)).
-//   3. scan_final:   every chunk re-scanned from H_c, writing y; the last chunk writes the caches.
-#include <hip/hip_runtime.h>
-
-#include <cstdint>
-
+// What is computed follows "Axon-SSM: Selective State Space Model for Apple Silicon" (formulas in
+// axon_device.h); the decode step is the section "Autoregressive decoding": one token per batch
+// row, with the conv window (the last K-1 raw inputs) and the hidden state carried in place.
+#include "axon_device.h"
 #include "axon_internal.h"
 
 namespace axon {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kWave = 64;
-
-using bf16_bits = uint16_t;
-
-__device__ __forceinline__ float load_act(const float* p, int64_t i) { return p[i]; }
-__device__ __forceinline__ float load_act(const bf16_bits* p, int64_t i) {
-  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
-}
-// Wave-uniform reads of data no kernel writes (the B_t / C_t rows): through the constant address
-// space, so the compiler issues scalar loads and the values arrive in SGPRs.
-__device__ __forceinline__ float load_uniform(const float* p, int64_t i) {
-  return ((const __attribute__((address_space(4))) float*)p)[i];
-}
-__device__ __forceinline__ float load_uniform(const bf16_bits* p, int64_t i) {
-  const auto* q = (const __attribute__((address_space(4))) bf16_bits*)p;
-  return __uint_as_float(static_cast<uint32_t>(q[i]) << 16);
-}
-__device__ __forceinline__ void store_act(float* p, int64_t i, float v) { p[i] = v; }
-__device__ __forceinline__ void store_act(bf16_bits* p, int64_t i, float v) {
-  // round to nearest, ties to even
-  uint32_t u = __float_as_uint(v);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  p[i] = static_cast<bf16_bits>(u >> 16);
-}
-
-// A_n * log2(e) with A_n = -exp(A_log_n), so that exp(dt A_n) = exp2(dt * rate).
-__device__ __forceinline__ float decay_rate_log2(float a_log) { return -expf(a_log) * kLog2e; }
-
-// dt = clip(softplus(v), lo, hi); softplus(v) = max(v, 0) + log1p(exp(-|v|)) (no overflow, and
-// accurate where the result is tiny).
-__device__ __forceinline__ float step_size(float v, float lo, float hi) {
-  const float sp = fmaxf(v, 0.0f) + log1pf(__expf(-fabsf(v)));
-  return fminf(fmaxf(sp, lo), hi);
-}
-
-// SiLU(z) = z / (1 + exp(-z)).
-__device__ __forceinline__ float silu(float z) { return __fdividef(z, 1.0f + __expf(-z)); }
-
-struct ChunkArgs {
-  int64_t B, L, E, T, M;
-  const void *x, *z, *dt_raw, *Bm, *Cm;
-  const float *A_log, *D, *dt_bias, *conv_w, *conv_b;
-  float dt_min, dt_max;
-  const float* win_src;  // (B, 3, E) conv window before token 0; null = zeros
-  const float* h_src;    // M == 1: (B, E, N) state_in or null; M > 1: carry_in (M, B, E, N)
-  void* y;
-  float *cache_out, *state_out;
-  float *carry_h, *carry_s, *halo;
-};
-
-// Pass 1: for chunk c < M-1, the local scan from a zero state; keeps the chunk's carry.
-template <typename Act>
-__global__ __launch_bounds__(kWave) void scan_carry_kernel(ChunkArgs a) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * kWave + threadIdx.x;
-  if (e >= a.E) return;
-  const int64_t b = blockIdx.y;
-  const int64_t c = blockIdx.z;
-  const int64_t t0 = c * a.T;
-  const int64_t t1 = (t0 + a.T < a.L) ? t0 + a.T : a.L;
-  const Act* __restrict__ x = static_cast<const Act*>(a.x);
-  const Act* __restrict__ dtr = static_cast<const Act*>(a.dt_raw);
-  const Act* __restrict__ Bp = static_cast<const Act*>(a.Bm) + b * a.L * kState;
-
-  float rate[kState], h[kState];
-#pragma unroll
-  for (int n = 0; n < kState; ++n) {
-    rate[n] = decay_rate_log2(a.A_log[e * kState + n]);
-    h[n] = 0.0f;
-  }
-  const float w0 = a.conv_w[e * kConv + 0], w1 = a.conv_w[e * kConv + 1];
-  const float w2 = a.conv_w[e * kConv + 2], w3 = a.conv_w[e * kConv + 3];
-  const float cb = a.conv_b[e], dtb = a.dt_bias[e];
-
-  float x0, x1, x2;  // x_{t-3}, x_{t-2}, x_{t-1}
-  if (c == 0) {
-    const float* w = a.win_src;
-    x0 = w ? w[(b * kHalo + 0) * a.E + e] : 0.0f;
-    x1 = w ? w[(b * kHalo + 1) * a.E + e] : 0.0f;
-    x2 = w ? w[(b * kHalo + 2) * a.E + e] : 0.0f;
-    // Keep a copy of the incoming window: the final pass reads it from here, so the caller may
-    // update conv_cache in place.
-    a.halo[(b * kHalo + 0) * a.E + e] = x0;
-    a.halo[(b * kHalo + 1) * a.E + e] = x1;
-    a.halo[(b * kHalo + 2) * a.E + e] = x2;
-  } else {
-    x0 = load_act(x, (b * a.L + t0 - 3) * a.E + e);
-    x1 = load_act(x, (b * a.L + t0 - 2) * a.E + e);
-    x2 = load_act(x, (b * a.L + t0 - 1) * a.E + e);
-  }
-
-  float S = 0.0f;
-  for (int64_t t = t0; t < t1; ++t) {
-    const int64_t i = (b * a.L + t) * a.E + e;
-    const float xv = load_act(x, i);
-    const float u = fmaf(w3, xv, fmaf(w2, x2, fmaf(w1, x1, fmaf(w0, x0, cb))));
-    x0 = x1;
-    x1 = x2;
-    x2 = xv;
-    const float dt = step_size(load_act(dtr, i) + dtb, a.dt_min, a.dt_max);
-    const float dtu = dt * u;
-    S += dt;
-#pragma unroll
-    for (int n = 0; n < kState; ++n) {
-      const float abar = __builtin_amdgcn_exp2f(dt * rate[n]);
-      h[n] = fmaf(abar, h[n], dtu * load_uniform(Bp, t * kState + n));
-    }
-  }
-  const int64_t be = (c * a.B + b) * a.E + e;
-#pragma unroll
-  for (int n = 0; n < kState; ++n) a.carry_h[be * kState + n] = h[n];
-  a.carry_s[be] = S;
-}
-
-// Pass 2: one thread per (b, e, n); walks the M chunks in order.
+// Carry combine of the time-chunked prefill: one thread per (b, e, n) walks the M chunks in
+// order, H_0 = state_in, H_{c+1} = exp(A S_c) H_c + h_c, where S_c is the chunk's sum of dt
+// (the product of the chunk's decays exp(dt A)) and h_c its local final state from zero.
 __global__ __launch_bounds__(256) void carry_combine_kernel(int64_t B, int64_t E, int64_t M,
                                                             const float* __restrict__ A_log,
                                                             const float* __restrict__ state_in,
@@ -163,75 +33,6 @@ __global__ __launch_bounds__(256) void carry_combine_kernel(int64_t B, int64_t E
       const float decay = __builtin_amdgcn_exp2f(rate * carry_s[c * B * E + be]);
       H = fmaf(decay, H, carry_h[c * total + idx]);
     }
-  }
-}
-
-// Pass 3 (or the only pass when M == 1): scan each chunk from its true initial state.
-template <typename Act>
-__global__ __launch_bounds__(kWave) void scan_final_kernel(ChunkArgs a) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * kWave + threadIdx.x;
-  if (e >= a.E) return;
-  const int64_t b = blockIdx.y;
-  const int64_t c = blockIdx.z;
-  const int64_t t0 = c * a.T;
-  const int64_t t1 = (t0 + a.T < a.L) ? t0 + a.T : a.L;
-  const Act* __restrict__ x = static_cast<const Act*>(a.x);
-  const Act* __restrict__ zp = static_cast<const Act*>(a.z);
-  const Act* __restrict__ dtr = static_cast<const Act*>(a.dt_raw);
-  const Act* __restrict__ Bp = static_cast<const Act*>(a.Bm) + b * a.L * kState;
-  const Act* __restrict__ Cp = static_cast<const Act*>(a.Cm) + b * a.L * kState;
-  Act* __restrict__ y = static_cast<Act*>(a.y);
-
-  float rate[kState], h[kState];
-  const float* hs = (a.M == 1) ? a.h_src : a.h_src + (c * a.B + b) * a.E * kState;
-  const int64_t hrow = (a.M == 1) ? (b * a.E + e) * kState : e * kState;
-#pragma unroll
-  for (int n = 0; n < kState; ++n) {
-    rate[n] = decay_rate_log2(a.A_log[e * kState + n]);
-    h[n] = hs ? hs[hrow + n] : 0.0f;
-  }
-  const float w0 = a.conv_w[e * kConv + 0], w1 = a.conv_w[e * kConv + 1];
-  const float w2 = a.conv_w[e * kConv + 2], w3 = a.conv_w[e * kConv + 3];
-  const float cb = a.conv_b[e], dtb = a.dt_bias[e], Dv = a.D[e];
-
-  float x0, x1, x2;
-  if (c == 0) {
-    const float* w = a.win_src;
-    x0 = w ? w[(b * kHalo + 0) * a.E + e] : 0.0f;
-    x1 = w ? w[(b * kHalo + 1) * a.E + e] : 0.0f;
-    x2 = w ? w[(b * kHalo + 2) * a.E + e] : 0.0f;
-  } else {
-    x0 = load_act(x, (b * a.L + t0 - 3) * a.E + e);
-    x1 = load_act(x, (b * a.L + t0 - 2) * a.E + e);
-    x2 = load_act(x, (b * a.L + t0 - 1) * a.E + e);
-  }
-
-  for (int64_t t = t0; t < t1; ++t) {
-    const int64_t i = (b * a.L + t) * a.E + e;
-    const float xv = load_act(x, i);
-    const float u = fmaf(w3, xv, fmaf(w2, x2, fmaf(w1, x1, fmaf(w0, x0, cb))));
-    x0 = x1;
-    x1 = x2;
-    x2 = xv;
-    const float dt = step_size(load_act(dtr, i) + dtb, a.dt_min, a.dt_max);
-    const float dtu = dt * u;
-    float acc = 0.0f;
-#pragma unroll
-    for (int n = 0; n < kState; ++n) {
-      const float abar = __builtin_amdgcn_exp2f(dt * rate[n]);
-      h[n] = fmaf(abar, h[n], dtu * load_uniform(Bp, t * kState + n));
-      acc = fmaf(load_uniform(Cp, t * kState + n), h[n], acc);
-    }
-    acc = fmaf(Dv, u, acc);
-    store_act(y, i, acc * silu(load_act(zp, i)));
-  }
-
-  if (c == a.M - 1) {
-#pragma unroll
-    for (int n = 0; n < kState; ++n) a.state_out[(b * a.E + e) * kState + n] = h[n];
-    a.cache_out[(b * kHalo + 0) * a.E + e] = x0;
-    a.cache_out[(b * kHalo + 1) * a.E + e] = x1;
-    a.cache_out[(b * kHalo + 2) * a.E + e] = x2;
   }
 }
 
@@ -279,7 +80,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const float dtu = dt * u;
 
   float4* sp = reinterpret_cast<float4*>(a.state + (b * a.E + e) * kState + 4 * q);
-  float4 h4 = *sp;
+  const float4 h4 = *sp;
   float h[4] = {h4.x, h4.y, h4.z, h4.w};
   float p = 0.0f;
 #pragma unroll
@@ -302,63 +103,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       a.cache[(b * kHalo + q) * a.E + e] = nv;
     }
   }
-}
-
-template <typename T>
-T* at_offset(void* base, size_t off) {
-  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
-}
-
-template <typename Act>
-int launch_prefill_t(const PrefillLaunch& p, const PrefillPlan& plan, hipStream_t s) {
-  ChunkArgs a{};
-  a.B = p.batch;
-  a.L = p.seqlen;
-  a.E = p.d_inner;
-  a.T = plan.chunk_len;
-  a.M = plan.chunks;
-  a.x = p.x;
-  a.z = p.z;
-  a.dt_raw = p.dt_raw;
-  a.Bm = p.B;
-  a.Cm = p.C;
-  a.A_log = p.A_log;
-  a.D = p.D;
-  a.dt_bias = p.dt_bias;
-  a.conv_w = p.conv_w;
-  a.conv_b = p.conv_b;
-  a.dt_min = p.dt_min;
-  a.dt_max = p.dt_max;
-  a.y = p.y;
-  a.cache_out = p.conv_cache_out;
-  a.state_out = p.ssm_state_out;
-  const dim3 block(kWave);
-  const unsigned gx = static_cast<unsigned>((p.d_inner + kWave - 1) / kWave);
-  if (plan.chunks == 1) {
-    a.win_src = p.conv_cache_in;
-    a.h_src = p.ssm_state_in;
-    hipLaunchKernelGGL(scan_final_kernel<Act>, dim3(gx, static_cast<unsigned>(p.batch), 1),
-                       block, 0, s, a);
-    return static_cast<int>(hipGetLastError());
-  }
-  a.carry_h = at_offset<float>(p.workspace, plan.off_carry_h);
-  a.carry_s = at_offset<float>(p.workspace, plan.off_carry_s);
-  a.halo = at_offset<float>(p.workspace, plan.off_halo);
-  float* carry_in = at_offset<float>(p.workspace, plan.off_carry_in);
-  a.win_src = p.conv_cache_in;
-  hipLaunchKernelGGL(scan_carry_kernel<Act>,
-                     dim3(gx, static_cast<unsigned>(p.batch), static_cast<unsigned>(plan.chunks - 1)),
-                     block, 0, s, a);
-  const int64_t total = p.batch * p.d_inner * kState;
-  hipLaunchKernelGGL(carry_combine_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
-                     dim3(256), 0, s, p.batch, p.d_inner, plan.chunks, p.A_log, p.ssm_state_in,
-                     a.carry_h, a.carry_s, carry_in);
-  a.win_src = a.halo;
-  a.h_src = carry_in;
-  hipLaunchKernelGGL(scan_final_kernel<Act>,
-                     dim3(gx, static_cast<unsigned>(p.batch), static_cast<unsigned>(plan.chunks)),
-                     block, 0, s, a);
-  return static_cast<int>(hipGetLastError());
 }
 
 template <typename Act>
@@ -389,6 +133,14 @@ int launch_decode_t(const DecodeLaunch& p, hipStream_t s) {
 
 }  // namespace
 
+void launch_carry_combine(int64_t B, int64_t E, int64_t M, const float* A_log,
+                          const float* state_in, const float* carry_h, const float* carry_s,
+                          float* carry_in, hipStream_t s) {
+  const int64_t total = B * E * kState;
+  hipLaunchKernelGGL(carry_combine_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
+                     dim3(256), 0, s, B, E, M, A_log, state_in, carry_h, carry_s, carry_in);
+}
+
 int launch_prefill(const PrefillLaunch& p, const PrefillPlan& plan, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.seqlen == 0) {
@@ -404,7 +156,7 @@ int launch_prefill(const PrefillLaunch& p, const PrefillPlan& plan, void* stream
     }
     return static_cast<int>(hipGetLastError());
   }
-  return p.act_bf16 ? launch_prefill_t<bf16_bits>(p, plan, s) : launch_prefill_t<float>(p, plan, s);
+  return launch_row_scan(p, plan, stream);
 }
 
 int launch_decode(const DecodeLaunch& p, void* stream) {

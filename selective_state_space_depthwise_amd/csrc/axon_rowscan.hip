@@ -1,0 +1,545 @@
+// Row-split selective scan for gfx950: the prefill kernel.
+//
+// What is computed is the Axon-SSM layer of "Axon-SSM: Selective State Space Model for Apple
+// Silicon" (per-token formulas in axon_device.h): causal depthwise conv, dt, the diagonal
+// recurrence h = exp(dt A) h + dt B u, the readout C . h + D u and the SiLU(z) gate.
+//
+// Work split. A wave covers 16 channels (lane column c = lane % 16) and 4 lane rows
+// (q = lane / 16); W waves share the same 16 channels, so a channel's 16 states are spread over
+// the 4*W (row, wave) pairs, SPL = 4 / W states per lane. Shapes with few channels (1 x 7680) use
+// W = 4: one state per lane and two waves per SIMD, without cutting the sequence into chunks
+// (which would cost a second pass of exponentials); every exp(dt A) is evaluated exactly once.
+//
+// Per token and lane the state update is 5 VALU instructions per state: dt * rate, exp2, the
+// input dtu * B (B broadcast within the lane row by DPP row_newbcast from a register holding
+// 16 / SPL tokens x SPL states of B), the fma into h, and the readout product C * h (C broadcast
+// the same way). The products of 4 tokens are summed over the 4 lane rows by a transpose-reduce
+// with v_permlane32_swap / v_permlane16_swap (6 VALU instructions per 4 tokens), which leaves
+// token 4k + q of the wave's partial output in row q of register R_k. The W waves add their
+// partials through LDS; the wave that computed a token's prologue finishes it (skip term, gate,
+// store).
+//
+// Per (token, channel) the prologue computes u (conv) and dt once and shares (dt, dt*u) through
+// LDS. Inputs are prefetched into registers two tiles ahead.
+//
+// Inline assembly holds only VALU instructions (no memory access). Hazards are handled by
+// instruction order: in every block at least two VALU instructions of the block precede the first
+// DPP instruction, so every operand of a DPP instruction was written two or more instructions
+// earlier whatever the compiler placed before the block; every v_exp result is consumed at least
+// one instruction later. A token's readout products are computed one block late, so the state they
+// read is old enough for DPP; the products of a tile's last token are taken after an s_nop 1, and
+// that block ends with an s_nop 1 before any instruction the compiler places after it.
+#include "axon_device.h"
+#include "axon_internal.h"
+
+namespace axon {
+namespace {
+
+constexpr int kGroups = 2;  // 16-channel groups per workgroup
+
+// Tokens per tile: 32 where a lane holds one state (more work between barriers), 16 otherwise
+// (the register budget of 4 states per lane).
+template <int W>
+constexpr int tile_tokens() {
+  return W == 4 ? 32 : 16;
+}
+
+struct RowArgs {
+  int64_t B, L, E, T;
+  const void *x, *z, *dt_raw, *Bm, *Cm;
+  const float *A_log, *D, *dt_bias, *conv_w, *conv_b;
+  float dt_min, dt_max;
+  const float* win_src;     // (B, 3, E) conv inputs before token 0, or null (zeros)
+  const float* h_src;       // initial states (see h_chunk_stride), or null (zeros)
+  int64_t h_chunk_stride;   // elements between chunks in h_src
+  int64_t chunks;
+  void* y;
+  float *state_out, *cache_out;
+  float *carry_h, *carry_s, *halo;
+};
+
+// ---- token step ------------------------------------------------------------------------------
+// Block for token tau, in this order:
+//   A  an_i = dtn * rate_i             (decay argument of token tau+1, if any)
+//   D  an_i = exp2(an_i)
+//   B  b_i = dtu * bcast(RB, k_i)
+//   C  pp_i = bcast(RCp, kp_i) * h_i   (readout products of token tau-1: h is its state)
+//   E  b_i += a_i * h_i                (a: token tau's decay from the previous block; b is the
+//                                       new state)
+// Computing the decays one block ahead keeps the exp2 latency off the state chain.
+
+#define AXON_BC(dst, src, mul, k)                                                             \
+  "v_mul_f32_dpp %[" #dst "], %[" #src "], %[" #mul "] row_newbcast:%[" #k                   \
+  "] row_mask:0xf bank_mask:0xf\n\t"
+#define AXON_A1(i) "v_mul_f32 %[n" #i "], %[dtn], %[r" #i "]\n\t"
+#define AXON_D1(i) "v_exp_f32 %[n" #i "], %[n" #i "]\n\t"
+#define AXON_E1(i) "v_fmac_f32 %[b" #i "], %[a" #i "], %[h" #i "]\n\t"
+
+#define AXON_AD1 AXON_A1(0) AXON_D1(0)
+#define AXON_AD2 AXON_A1(0) AXON_A1(1) AXON_D1(0) AXON_D1(1)
+#define AXON_AD4 AXON_A1(0) AXON_A1(1) AXON_A1(2) AXON_A1(3) AXON_D1(0) AXON_D1(1) AXON_D1(2) AXON_D1(3)
+#define AXON_B1 AXON_BC(b0, RB, dtu, k0)
+#define AXON_B2 AXON_BC(b0, RB, dtu, k0) AXON_BC(b1, RB, dtu, k1)
+#define AXON_B4 AXON_BC(b0, RB, dtu, k0) AXON_BC(b1, RB, dtu, k1) AXON_BC(b2, RB, dtu, k2) AXON_BC(b3, RB, dtu, k3)
+#define AXON_C1 AXON_BC(p0, RCp, h0, kp0)
+#define AXON_C2 AXON_BC(p0, RCp, h0, kp0) AXON_BC(p1, RCp, h1, kp1)
+#define AXON_C4                                                                           \
+  AXON_BC(p0, RCp, h0, kp0) AXON_BC(p1, RCp, h1, kp1) AXON_BC(p2, RCp, h2, kp2)             \
+  AXON_BC(p3, RCp, h3, kp3)
+#define AXON_E1S AXON_E1(0)
+#define AXON_E2S AXON_E1(0) AXON_E1(1)
+#define AXON_E4S AXON_E1(0) AXON_E1(1) AXON_E1(2) AXON_E1(3)
+
+#define AXON_OUTB1 [b0] "=&v"(b[0])
+#define AXON_OUTB2 [b0] "=&v"(b[0]), [b1] "=&v"(b[1])
+#define AXON_OUTB4 [b0] "=&v"(b[0]), [b1] "=&v"(b[1]), [b2] "=&v"(b[2]), [b3] "=&v"(b[3])
+#define AXON_OUTN1 , [n0] "=&v"(an[0])
+#define AXON_OUTN2 , [n0] "=&v"(an[0]), [n1] "=&v"(an[1])
+#define AXON_OUTN4 , [n0] "=&v"(an[0]), [n1] "=&v"(an[1]), [n2] "=&v"(an[2]), [n3] "=&v"(an[3])
+#define AXON_OUTP1 , [p0] "=&v"(pp[0])
+#define AXON_OUTP2 , [p0] "=&v"(pp[0]), [p1] "=&v"(pp[1])
+#define AXON_OUTP4 , [p0] "=&v"(pp[0]), [p1] "=&v"(pp[1]), [p2] "=&v"(pp[2]), [p3] "=&v"(pp[3])
+#define AXON_IN_COMMON [dtn] "v"(dtn), [dtu] "v"(dtu), [RB] "v"(RB), [RCp] "v"(RCp)
+#define AXON_IN1 , [r0] "v"(r[0]), [a0] "v"(ac[0]), [h0] "v"(h[0]), [k0] "i"(K), [kp0] "i"(KP)
+#define AXON_IN2                                                                          \
+  , [r0] "v"(r[0]), [r1] "v"(r[1]), [a0] "v"(ac[0]), [a1] "v"(ac[1]), [h0] "v"(h[0]),    \
+      [h1] "v"(h[1]), [k0] "i"(K), [k1] "i"(K + 1), [kp0] "i"(KP), [kp1] "i"(KP + 1)
+#define AXON_IN4                                                                              \
+  , [r0] "v"(r[0]), [r1] "v"(r[1]), [r2] "v"(r[2]), [r3] "v"(r[3]), [a0] "v"(ac[0]),         \
+      [a1] "v"(ac[1]), [a2] "v"(ac[2]), [a3] "v"(ac[3]), [h0] "v"(h[0]), [h1] "v"(h[1]),     \
+      [h2] "v"(h[2]), [h3] "v"(h[3]), [k0] "i"(K), [k1] "i"(K + 1), [k2] "i"(K + 2),         \
+      [k3] "i"(K + 3), [kp0] "i"(KP), [kp1] "i"(KP + 1), [kp2] "i"(KP + 2), [kp3] "i"(KP + 3)
+
+// One token. ac: this token's decays; an (out, kNext): the next token's decays from dtn.
+// kPrev: also the readout products of the previous token. Every block starts with two or more
+// VALU instructions before its first DPP instruction (the A/D pair, or an s_nop 1 without it).
+template <int SPL, int K, int KP, bool kPrev, bool kNext>
+__device__ __forceinline__ void step(float dtn, float dtu, const float (&r)[SPL],
+                                     const float (&ac)[SPL], float RB, float RCp,
+                                     float (&h)[SPL], float (&an)[SPL], float (&pp)[SPL]) {
+  float b[SPL];
+#define AXON_STEP(N)                                                                            \
+  if constexpr (kNext && kPrev)                                                                 \
+    asm(AXON_AD##N AXON_B##N AXON_C##N AXON_E##N##S                                             \
+        : AXON_OUTB##N AXON_OUTN##N AXON_OUTP##N : AXON_IN_COMMON AXON_IN##N);                  \
+  else if constexpr (kNext)                                                                     \
+    asm(AXON_AD##N AXON_B##N AXON_E##N##S : AXON_OUTB##N AXON_OUTN##N : AXON_IN_COMMON AXON_IN##N); \
+  else if constexpr (kPrev)                                                                     \
+    asm("s_nop 1\n\t" AXON_B##N AXON_C##N AXON_E##N##S                                          \
+        : AXON_OUTB##N AXON_OUTP##N : AXON_IN_COMMON AXON_IN##N);                               \
+  else                                                                                          \
+    asm("s_nop 1\n\t" AXON_B##N AXON_E##N##S : AXON_OUTB##N : AXON_IN_COMMON AXON_IN##N);
+  if constexpr (SPL == 1) {
+    AXON_STEP(1)
+  } else if constexpr (SPL == 2) {
+    AXON_STEP(2)
+  } else {
+    AXON_STEP(4)
+  }
+#undef AXON_STEP
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) h[i] = b[i];
+}
+
+// Decays of a tile's first token: exp2(dt * rate), in a block of its own.
+template <int SPL>
+__device__ __forceinline__ void first_decay(float dtn, const float (&r)[SPL], float (&an)[SPL]) {
+  if constexpr (SPL == 1) {
+    asm(AXON_AD1 : [n0] "=&v"(an[0]) : [dtn] "v"(dtn), [r0] "v"(r[0]));
+  } else if constexpr (SPL == 2) {
+    asm(AXON_AD2 : [n0] "=&v"(an[0]), [n1] "=&v"(an[1]) : [dtn] "v"(dtn), [r0] "v"(r[0]), [r1] "v"(r[1]));
+  } else {
+    asm(AXON_AD4
+        : [n0] "=&v"(an[0]), [n1] "=&v"(an[1]), [n2] "=&v"(an[2]), [n3] "=&v"(an[3])
+        : [dtn] "v"(dtn), [r0] "v"(r[0]), [r1] "v"(r[1]), [r2] "v"(r[2]), [r3] "v"(r[3]));
+  }
+}
+
+// Readout products of a tile's last token (its state was written by the block just before).
+template <int SPL, int KP>
+__device__ __forceinline__ void flush(float RCp, const float (&h)[SPL], float (&pp)[SPL]) {
+  if constexpr (SPL == 1) {
+    asm("s_nop 1\n\t" AXON_C1 "s_nop 1"
+        : [p0] "=&v"(pp[0]) : [RCp] "v"(RCp), [h0] "v"(h[0]), [kp0] "i"(KP));
+  } else if constexpr (SPL == 2) {
+    asm("s_nop 1\n\t" AXON_C2 "s_nop 1"
+        : [p0] "=&v"(pp[0]), [p1] "=&v"(pp[1])
+        : [RCp] "v"(RCp), [h0] "v"(h[0]), [h1] "v"(h[1]), [kp0] "i"(KP), [kp1] "i"(KP + 1));
+  } else {
+    asm("s_nop 1\n\t" AXON_C4 "s_nop 1"
+        : [p0] "=&v"(pp[0]), [p1] "=&v"(pp[1]), [p2] "=&v"(pp[2]), [p3] "=&v"(pp[3])
+        : [RCp] "v"(RCp), [h0] "v"(h[0]), [h1] "v"(h[1]), [h2] "v"(h[2]), [h3] "v"(h[3]),
+          [kp0] "i"(KP), [kp1] "i"(KP + 1), [kp2] "i"(KP + 2), [kp3] "i"(KP + 3));
+  }
+}
+
+template <int SPL>
+__device__ __forceinline__ float lane_sum(const float (&pp)[SPL]) {
+  float p = pp[0];
+#pragma unroll
+  for (int i = 1; i < SPL; ++i) p += pp[i];
+  return p;
+}
+
+// The tokens of a tile. RB[j] / RC[j] hold B / C of tokens j*16/SPL .. (j+1)*16/SPL - 1 for
+// this row's SPL states (lane position tau_local * SPL + i). dd holds (dt, dt*u) of the tile's
+// tokens for this lane's channel, two tokens per float4. P[tau] receives the lane's readout
+// product of token tau; ac carries the current token's decays from block to block.
+template <int SPL, bool kCarry, int TAU, int kTile>
+__device__ __forceinline__ void scan_tile_from(const float4 (&dd)[kTile / 2],
+                                               const float (&rate)[SPL],
+                                               const float (&RB)[kTile * SPL / 16],
+                                               const float (&RC)[kTile * SPL / 16],
+                                               float (&h)[SPL], float (&ac)[SPL],
+                                               float (&P)[kTile], float& S) {
+  constexpr int TPR = 16 / SPL;  // tokens per broadcast register
+  constexpr int J = TAU / TPR;
+  constexpr int K = (TAU % TPR) * SPL;
+  constexpr int JP = (TAU > 0 ? TAU - 1 : 0) / TPR;
+  constexpr int KP = ((TAU > 0 ? TAU - 1 : 0) % TPR) * SPL;
+  constexpr int TN = TAU + 1 < kTile ? TAU + 1 : TAU;
+  const float dtu = (TAU & 1) ? dd[TAU / 2].w : dd[TAU / 2].y;
+  const float dtn = (TN & 1) ? dd[TN / 2].z : dd[TN / 2].x;
+  if constexpr (TAU == 0) {
+    const float dt0 = dd[0].x;
+    first_decay<SPL>(dt0, rate, ac);
+    if constexpr (kCarry) S += dt0;
+  }
+  if constexpr (kCarry && TAU + 1 < kTile) S += dtn;
+  float pp[SPL], an[SPL];
+  constexpr bool kPrev = !kCarry && TAU >= 1;
+  constexpr bool kNext = TAU + 1 < kTile;
+  step<SPL, K, KP, kPrev, kNext>(dtn, dtu, rate, ac, RB[J], RC[JP], h, an, pp);
+  if constexpr (kPrev) P[TAU - 1] = lane_sum<SPL>(pp);
+  if constexpr (kNext) {
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) ac[i] = an[i];
+    scan_tile_from<SPL, kCarry, TAU + 1, kTile>(dd, rate, RB, RC, h, ac, P, S);
+  } else if constexpr (!kCarry) {
+    flush<SPL, ((kTile - 1) % TPR) * SPL>(RC[kTile * SPL / 16 - 1], h, pp);
+    P[kTile - 1] = lane_sum<SPL>(pp);
+  }
+}
+
+// Sum of four tokens' products over the 4 lane rows: on return, row q holds token q's sum.
+__device__ __forceinline__ float rows_reduce4(float p0, float p1, float p2, float p3) {
+  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2),
+                                                    false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3),
+                                                    false, false);
+  const float a = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+  const float b = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// Inputs of one tile for this lane, loaded ahead of use. The lane's prologue tokens are
+// ts + 4k + q for k = w*TPL .. w*TPL + TPL - 1; B / C registers as for scan_tile_from.
+template <int SPL, int TPL, int kTile>
+struct TileIn {
+  static constexpr int NR = kTile * SPL / 16;  // B (and C) registers per tile
+  float xw[TPL][4];  // x at t-3 .. t for each prologue token t
+  float dr[TPL];
+  float zz[TPL];
+  float RB[NR], RC[NR];
+};
+
+template <typename Act, int W, bool kCarry>
+__global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
+  constexpr int SPL = 4 / W;  // states per lane
+  constexpr int kTile = tile_tokens<W>();
+  constexpr int kDtStride = 2 * kTile + 4;  // floats per channel in the dt / dtu tile (padded)
+  constexpr int TPL = kTile / (4 * W);  // prologue / epilogue tokens per lane per tile
+  constexpr int NW = W * kGroups;
+  constexpr int TPR = 16 / SPL;         // tokens per B / C register
+  constexpr int NR = kTile * SPL / 16;  // B / C registers per tile
+  constexpr int NX = kTile / 16;        // float4 groups of reduced outputs per lane
+  __shared__ __attribute__((aligned(16))) float s_dt[2][kGroups * 16][kDtStride];
+  __shared__ float4 s_ex[2][NW][NX][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int grp = wid / W;
+  const int w = wid % W;
+  const int q = lane >> 4;
+  const int c = lane & 15;
+  const int slot = grp * 16 + c;
+  const int64_t b = blockIdx.y;
+  const int64_t e_raw = static_cast<int64_t>(blockIdx.x) * (kGroups * 16) + slot;
+  const bool valid = e_raw < a.E;
+  const int64_t e = valid ? e_raw : a.E - 1;
+  const int g = w * 4 + q;  // this lane's state group: states g*SPL .. g*SPL + SPL - 1
+  const int64_t chunk = blockIdx.z;
+  const int64_t tb = chunk * a.T;
+  const int64_t te = (tb + a.T < a.L) ? tb + a.T : a.L;
+  const int64_t L = a.L, E = a.E;
+
+  const Act* __restrict__ xp = static_cast<const Act*>(a.x);
+  const Act* __restrict__ zp = static_cast<const Act*>(a.z);
+  const Act* __restrict__ dtrp = static_cast<const Act*>(a.dt_raw);
+  const Act* __restrict__ Bp = static_cast<const Act*>(a.Bm) + b * L * kState;
+  const Act* __restrict__ Cp = static_cast<const Act*>(a.Cm) + b * L * kState;
+
+  float rate[SPL], h[SPL];
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const int n = g * SPL + i;
+    rate[i] = valid ? decay_rate_log2(a.A_log[e * kState + n]) : 0.0f;
+    h[i] = (a.h_src && valid) ? a.h_src[chunk * a.h_chunk_stride + (b * E + e) * kState + n]
+                              : 0.0f;
+  }
+  const float w0 = a.conv_w[e * kConv + 0], w1 = a.conv_w[e * kConv + 1];
+  const float w2 = a.conv_w[e * kConv + 2], w3 = a.conv_w[e * kConv + 3];
+  const float cb = a.conv_b[e], dtb = a.dt_bias[e], Dv = a.D[e];
+
+  if constexpr (kCarry) {
+    // Chunk 0 keeps a copy of the incoming conv window: the final pass reads it from the
+    // workspace, so the caller may update conv_cache in place.
+    if (chunk == 0 && w == 0 && q == 0 && valid) {
+#pragma unroll
+      for (int j = 0; j < kHalo; ++j)
+        a.halo[(b * kHalo + j) * E + e] = a.win_src ? a.win_src[(b * kHalo + j) * E + e] : 0.0f;
+    }
+  }
+
+  auto load_x = [&](int64_t tt) -> float {
+    if (tt < 0) return a.win_src ? a.win_src[(b * kHalo + (tt + kHalo)) * E + e] : 0.0f;
+    return load_act(xp, (b * L + (tt < L ? tt : L - 1)) * E + e);
+  };
+  // This lane's elements of the (b, e) channel: token t at [t * E].
+  const Act* __restrict__ xl = xp + b * L * E + e;
+  const Act* __restrict__ dl = dtrp + b * L * E + e;
+  const Act* __restrict__ zl = zp + b * L * E + e;
+  auto load_tile = [&](int64_t ts, TileIn<SPL, TPL, kTile>& in) {
+    if (ts >= 3 && ts + kTile <= L) {
+      // Fast path (uniform branch): the tile and its conv halo lie inside the sequence.
+#pragma unroll
+      for (int r = 0; r < TPL; ++r) {
+        const int64_t t = ts + 4 * (w * TPL + r) + q;
+        const Act* px = xl + (t - 3) * E;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) in.xw[r][k] = load_act(px, k * E);
+        in.dr[r] = load_act(dl, t * E);
+        if constexpr (!kCarry) in.zz[r] = load_act(zl, t * E);
+      }
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        const int64_t tt = ts + j * TPR + c / SPL;
+        const int n = g * SPL + (c % SPL);
+        in.RB[j] = load_act(Bp, tt * kState + n);
+        if constexpr (!kCarry) in.RC[j] = load_act(Cp, tt * kState + n);
+      }
+      return;
+    }
+#pragma unroll
+    for (int r = 0; r < TPL; ++r) {
+      const int64_t t = ts + 4 * (w * TPL + r) + q;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) in.xw[r][k] = load_x(t - 3 + k);
+      const int64_t tt = t < L ? t : L - 1;
+      in.dr[r] = load_act(dl, tt * E);
+      if constexpr (!kCarry) in.zz[r] = load_act(zl, tt * E);
+    }
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      int64_t tt = ts + j * TPR + c / SPL;
+      tt = tt < L ? tt : L - 1;
+      const int n = g * SPL + (c % SPL);
+      in.RB[j] = load_act(Bp, tt * kState + n);
+      if constexpr (!kCarry) in.RC[j] = load_act(Cp, tt * kState + n);
+    }
+  };
+  // dt and dt*u of this lane's prologue tokens into the LDS tile; u is kept for the skip term.
+  auto prologue = [&](int64_t ts, const TileIn<SPL, TPL, kTile>& in, int buf, float (&u)[TPL]) {
+#pragma unroll
+    for (int r = 0; r < TPL; ++r) {
+      const int tau = 4 * (w * TPL + r) + q;
+      const float uu = fmaf(w3, in.xw[r][3],
+                            fmaf(w2, in.xw[r][2], fmaf(w1, in.xw[r][1], fmaf(w0, in.xw[r][0], cb))));
+      const bool ok = valid && (ts + tau < te);
+      const float dt = ok ? step_size(in.dr[r] + dtb, a.dt_min, a.dt_max) : 0.0f;
+      *reinterpret_cast<float2*>(&s_dt[buf][slot][2 * tau]) = make_float2(dt, dt * uu);
+      u[r] = uu;
+    }
+  };
+
+  const int64_t ntiles = (te - tb + kTile - 1) / kTile;
+  // Two static ring slots (a dynamically indexed register array would live in scratch memory):
+  // the loop body handles tiles in pairs with the slots' roles swapped.
+  TileIn<SPL, TPL, kTile> ring0, ring1;
+  float u_cur[TPL], z_cur[TPL], rb[NR], rc[NR];
+  load_tile(tb, ring0);
+  if (ntiles > 1) load_tile(tb + kTile, ring1);
+  prologue(tb, ring0, 0, u_cur);
+#pragma unroll
+  for (int r = 0; r < TPL; ++r) z_cur[r] = ring0.zz[r];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    rb[j] = ring0.RB[j];
+    rc[j] = ring0.RC[j];
+  }
+  __syncthreads();
+
+  float S = 0.0f;
+  Act* __restrict__ yp = static_cast<Act*>(a.y);
+  // Tile k: its inputs came from `mine`, which then receives tile k+2; tile k+1 (loaded one tile
+  // ago into `other`) gets its prologue after the scan of tile k.
+  auto do_tile = [&](int64_t k, TileIn<SPL, TPL, kTile>& mine, const TileIn<SPL, TPL, kTile>& other) {
+    const int64_t ts = tb + k * kTile;
+    const int buf = static_cast<int>(k & 1);
+    if (k + 2 < ntiles) load_tile(ts + 2 * kTile, mine);
+    float4 dd[kTile / 2];
+#pragma unroll
+    for (int i = 0; i < kTile / 2; ++i)
+      dd[i] = *reinterpret_cast<const float4*>(&s_dt[buf][slot][4 * i]);
+    float P[kTile], ac[SPL];
+    scan_tile_from<SPL, kCarry, 0, kTile>(dd, rate, rb, rc, h, ac, P, S);
+
+    const bool has_next = k + 1 < ntiles;
+    float u_next[TPL];
+    if (has_next) prologue(ts + kTile, other, buf ^ 1, u_next);
+    if constexpr (!kCarry) {
+#pragma unroll
+      for (int x4 = 0; x4 < NX; ++x4) {
+        const float* p = P + 16 * x4;
+        float4 R;
+        R.x = rows_reduce4(p[0], p[1], p[2], p[3]);
+        R.y = rows_reduce4(p[4], p[5], p[6], p[7]);
+        R.z = rows_reduce4(p[8], p[9], p[10], p[11]);
+        R.w = rows_reduce4(p[12], p[13], p[14], p[15]);
+        s_ex[buf][wid][x4][lane] = R;
+      }
+    }
+    __syncthreads();
+    if constexpr (!kCarry) {
+      // This wave finishes tokens ts + 4k + q, k = w*TPL .. w*TPL + TPL - 1, of channel e: the
+      // tokens its prologue computed.
+#pragma unroll
+      for (int r = 0; r < TPL; ++r) {
+        const int kk = w * TPL + r;
+        float ysum = 0.0f;
+#pragma unroll
+        for (int v = 0; v < W; ++v)
+          ysum += reinterpret_cast<const float*>(&s_ex[buf][grp * W + v][kk >> 2][lane])[kk & 3];
+        const int64_t t = ts + 4 * kk + q;
+        if (valid && t < te) {
+          const float yv = fmaf(Dv, u_cur[r], ysum) * silu(z_cur[r]);
+          store_act(yp, (b * L + t) * E + e, yv);
+        }
+      }
+    }
+    if (has_next) {
+#pragma unroll
+      for (int r = 0; r < TPL; ++r) {
+        u_cur[r] = u_next[r];
+        z_cur[r] = other.zz[r];
+      }
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        rb[j] = other.RB[j];
+        rc[j] = other.RC[j];
+      }
+    }
+  };
+  for (int64_t k = 0; k < ntiles; k += 2) {
+    do_tile(k, ring0, ring1);
+    if (k + 1 < ntiles) do_tile(k + 1, ring1, ring0);
+  }
+
+  if (!valid) return;
+  if constexpr (kCarry) {
+    const int64_t be = (chunk * a.B + b) * E + e;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) a.carry_h[be * kState + g * SPL + i] = h[i];
+    if (w == 0 && q == 0) a.carry_s[be] = S;
+  } else if (chunk == a.chunks - 1) {
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) a.state_out[(b * E + e) * kState + g * SPL + i] = h[i];
+    if (w == 0 && q == 0) {
+      // Last K-1 inputs of [conv window, x]: read all three before writing (in-place caches).
+      float cv[kHalo];
+#pragma unroll
+      for (int j = 0; j < kHalo; ++j) cv[j] = load_x(L - kHalo + j);
+#pragma unroll
+      for (int j = 0; j < kHalo; ++j) a.cache_out[(b * kHalo + j) * E + e] = cv[j];
+    }
+  }
+}
+
+}  // namespace
+
+// Carry combine of the time-chunked prefill (axon_kernels.hip).
+void launch_carry_combine(int64_t B, int64_t E, int64_t M, const float* A_log,
+                          const float* state_in, const float* carry_h, const float* carry_s,
+                          float* carry_in, hipStream_t s);
+
+template <typename Act, int W>
+int launch_row_scan_t(const PrefillLaunch& p, const PrefillPlan& plan, hipStream_t s) {
+  RowArgs a{};
+  a.B = p.batch;
+  a.L = p.seqlen;
+  a.E = p.d_inner;
+  a.T = plan.chunk_len;
+  a.chunks = plan.chunks;
+  a.x = p.x;
+  a.z = p.z;
+  a.dt_raw = p.dt_raw;
+  a.Bm = p.B;
+  a.Cm = p.C;
+  a.A_log = p.A_log;
+  a.D = p.D;
+  a.dt_bias = p.dt_bias;
+  a.conv_w = p.conv_w;
+  a.conv_b = p.conv_b;
+  a.dt_min = p.dt_min;
+  a.dt_max = p.dt_max;
+  a.y = p.y;
+  a.state_out = p.ssm_state_out;
+  a.cache_out = p.conv_cache_out;
+  const dim3 block(64 * W * kGroups);
+  const unsigned gx = static_cast<unsigned>((p.d_inner + kGroups * 16 - 1) / (kGroups * 16));
+  const unsigned gy = static_cast<unsigned>(p.batch);
+  if (plan.chunks == 1) {
+    a.win_src = p.conv_cache_in;
+    a.h_src = p.ssm_state_in;
+    a.h_chunk_stride = 0;
+    hipLaunchKernelGGL((row_scan_kernel<Act, W, false>), dim3(gx, gy, 1), block, 0, s, a);
+    return static_cast<int>(hipGetLastError());
+  }
+  char* ws = static_cast<char*>(p.workspace);
+  a.carry_h = reinterpret_cast<float*>(ws + plan.off_carry_h);
+  a.carry_s = reinterpret_cast<float*>(ws + plan.off_carry_s);
+  a.halo = reinterpret_cast<float*>(ws + plan.off_halo);
+  float* carry_in = reinterpret_cast<float*>(ws + plan.off_carry_in);
+  a.win_src = p.conv_cache_in;
+  a.h_src = nullptr;
+  a.h_chunk_stride = 0;
+  hipLaunchKernelGGL((row_scan_kernel<Act, W, true>),
+                     dim3(gx, gy, static_cast<unsigned>(plan.chunks - 1)), block, 0, s, a);
+  launch_carry_combine(p.batch, p.d_inner, plan.chunks, p.A_log, p.ssm_state_in, a.carry_h,
+                       a.carry_s, carry_in, s);
+  a.win_src = a.halo;
+  a.h_src = carry_in;
+  a.h_chunk_stride = p.batch * p.d_inner * kState;
+  hipLaunchKernelGGL((row_scan_kernel<Act, W, false>),
+                     dim3(gx, gy, static_cast<unsigned>(plan.chunks)), block, 0, s, a);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_row_scan(const PrefillLaunch& p, const PrefillPlan& plan, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (plan.row_waves) {
+    case 1:
+      return p.act_bf16 ? launch_row_scan_t<bf16_bits, 1>(p, plan, s)
+                        : launch_row_scan_t<float, 1>(p, plan, s);
+    case 2:
+      return p.act_bf16 ? launch_row_scan_t<bf16_bits, 2>(p, plan, s)
+                        : launch_row_scan_t<float, 2>(p, plan, s);
+    default:
+      return p.act_bf16 ? launch_row_scan_t<bf16_bits, 4>(p, plan, s)
+                        : launch_row_scan_t<float, 4>(p, plan, s);
+  }
+}
+
+}  // namespace axon

@@ -14,11 +14,17 @@ constexpr int kVersion = 100;  // 0.1.0
 constexpr int64_t kMaxBatch = 65535;      // launch grid y dimension
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 
-// Below this many channel lanes the prefill cuts the sequence into chunks: 256 CUs x 4 SIMDs x
-// 2 waves of 64 lanes.
-constexpr int64_t kTargetLanes = 131072;
-constexpr int64_t kMinChunk = 64;
+// The prefill wants about one wave per SIMD (256 CUs x 4 SIMDs x 64 lanes = 65536). Below half of
+// that many (channel, state-group) lanes it also cuts the sequence into chunks of at least
+// kMinChunk tokens.
+constexpr int64_t kTargetLanes = 65536;
+constexpr int64_t kChunkBelowLanes = 32768;
+constexpr int64_t kMinChunk = 256;
 constexpr int64_t kMaxChunks = 64;
+// Channel counts from which the scan packs 4 (resp. 2) states per lane: a wave covers 16
+// channels x 16 / W states, and about two waves per SIMD (2048 waves) hide latency.
+constexpr int64_t kRowW1Channels = 32768;
+constexpr int64_t kRowW2Channels = 16384;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -88,15 +94,23 @@ namespace axon {
 PrefillPlan plan_prefill(int64_t batch, int64_t seqlen, int64_t d_inner) {
   PrefillPlan plan;
   const int64_t channels = batch * d_inner;
-  int64_t M = (kTargetLanes + channels - 1) / channels;
-  int64_t max_m = seqlen / kMinChunk;
-  if (max_m < 1) max_m = 1;
-  if (M > max_m) M = max_m;
-  if (M > kMaxChunks) M = kMaxChunks;
-  if (M < 1) M = 1;
+  // States per lane 4 / W: as many as the channel count allows while still giving the GPU about
+  // two waves per SIMD.
+  plan.row_waves = channels >= kRowW1Channels ? 1 : (channels >= kRowW2Channels ? 2 : 4);
+  const int64_t lanes = channels * 4 * plan.row_waves;
+  int64_t M = 1;
+  if (lanes < kChunkBelowLanes) {
+    M = (kTargetLanes + lanes - 1) / lanes;
+    int64_t max_m = seqlen / kMinChunk;
+    if (max_m < 1) max_m = 1;
+    if (M > max_m) M = max_m;
+    if (M > kMaxChunks) M = kMaxChunks;
+  }
+  // Chunks hold whole scan tiles (32 tokens with one state per lane, else 16).
+  const int64_t tile = plan.row_waves == 4 ? 32 : 16;
   int64_t T = (seqlen + M - 1) / M;
-  T = (T + 15) / 16 * 16;
-  if (T < 1) T = 1;
+  T = (T + tile - 1) / tile * tile;
+  if (T < tile) T = tile;
   M = (seqlen + T - 1) / T;
   if (M < 1) M = 1;
   plan.chunks = M;

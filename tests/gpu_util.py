@@ -5,6 +5,10 @@ Tolerances (element-wise, against the oracle run on the same rounded inputs):
   fp32 activations: |gpu - ref| <= 1e-4 * (1 + |ref|)
   bf16 activations: |gpu - ref| <= 2e-2 * (1 + |ref|)   (y is rounded to bf16; state stays fp32)
   conv cache: bit-exact (it holds copies of the inputs).
+Stress cases outside the workloads' distributions (fp32 with dt clipped at 50..100, where the
+states grow to ~100 and an output can be the small difference of large terms) use
+  |gpu - ref| <= 1e-4 * (1 + |ref| + mag),  mag = |SiLU(z)| * (sum_n |C h_n| + |D u|)
+from the oracle: fp32 rounding of the summed terms alone is of order 1e-7 * mag.
 """
 from __future__ import annotations
 
@@ -66,13 +70,13 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def assert_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str) -> None:
+def assert_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str, mag=None) -> None:
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite values from the GPU"
     err = np.abs(got - ref)
-    bound = tol * (1.0 + np.abs(ref))
+    bound = tol * (1.0 + np.abs(ref) + (0.0 if mag is None else np.asarray(mag, np.float64)))
     bad = err > bound
     if bad.any():
         idx = np.unravel_index(np.argmax(err / bound), err.shape)

@@ -63,12 +63,17 @@ def test_workspace_is_a_pure_function_of_shape():
     # enough channels to fill the GPU: no time chunks, no workspace
     assert A.workspace_bytes(_shape(1, 64, 32)) == 0
     assert A.workspace_bytes(_shape(64, 1, 7680)) == 0
+    assert A.workspace_bytes(_shape(1, 2048, 7680)) == 0      # fills the GPU by state splitting
+    assert A.workspace_bytes(_shape(2, 65536, 2048, True)) == 0
     # few channels, long sequence: chunked, workspace = carries + halo
-    ws1 = A.workspace_bytes(_shape(1, 2048, 7680))
-    assert ws1 == A.workspace_bytes(_shape(1, 2048, 7680))
-    assert ws1 > 2 * 16 * 4 * 7680  # at least two chunks of carries
+    ws1 = A.workspace_bytes(_shape(1, 8192, 256))
+    assert ws1 == A.workspace_bytes(_shape(1, 8192, 256))
+    assert ws1 > 2 * 16 * 4 * 256  # at least two chunks of carries
     assert ws1 % 256 == 0
-    assert A.workspace_bytes(_shape(2, 65536, 2048, True)) > 0
+    # empty and one-token sequences plan a single chunk, whatever the channel count
+    for bsz, e in ((1, 16), (1, 7680), (64, 7680)):
+        assert A.workspace_bytes(_shape(bsz, 0, e)) == 0
+        assert A.workspace_bytes(_shape(bsz, 1, e)) == 0
     # invalid shapes report 0
     assert A.workspace_bytes(_shape(d_state=8)) == 0
     assert A.workspace_bytes(_shape(batch=0)) == 0
@@ -131,7 +136,7 @@ def test_prefill_rejects_bad_params():
 
 
 def test_prefill_workspace_checks():
-    sh = _shape(1, 2048, 7680)
+    sh = _shape(1, 8192, 256)
     need = A.workspace_bytes(sh)
     assert need > 0
     assert _prefill(shape=sh, ws_bytes=need - 1) == A.AXON_ERR_WORKSPACE_TOO_SMALL
@@ -152,7 +157,7 @@ def test_prefill_rejects_forbidden_aliasing():
     assert _prefill(cout=b["x"]) == A.AXON_ERR_INVALID_ARGUMENT
     assert _prefill(sout=b["cout"]) == A.AXON_ERR_INVALID_ARGUMENT
     # workspace over an output
-    sh = _shape(1, 2048, 7680)
+    sh = _shape(1, 8192, 256)
     assert _prefill(shape=sh, ws=b["y"]) == A.AXON_ERR_INVALID_ARGUMENT
 
 
