@@ -38,7 +38,9 @@
  *   ssm_state       : (batch, d_inner, d_state) fp32 [AXON "Autoregressive decoding"]
  *
  * Supported shapes: d_state == 16, d_conv == 4 (the layer configuration table of [AXON]);
- * batch >= 1, d_inner >= 1, seqlen >= 0; batch*seqlen*d_inner < 2^62.
+ * batch >= 1, d_inner >= 1, seqlen >= 0 (else AXON_ERR_INVALID_ARGUMENT);
+ * batch <= 65535 and d_inner <= 2^24 (else AXON_ERR_UNSUPPORTED);
+ * batch*seqlen*d_inner*d_state <= 2^40 (else AXON_ERR_INVALID_ARGUMENT).
  * Activation dtype: fp32 or bf16 (bf16 outputs are rounded to nearest even from fp32).
  * State, cache and parameters are always fp32; the state recurrence runs in fp32.
  *
@@ -65,7 +67,7 @@ extern "C" {
 typedef enum {
   AXON_OK = 0,
   AXON_ERR_INVALID_ARGUMENT = 1,  /* null/misaligned pointer, bad size, forbidden aliasing */
-  AXON_ERR_UNSUPPORTED = 2,       /* d_state != 16, d_conv != 4, unknown dtype */
+  AXON_ERR_UNSUPPORTED = 2,       /* d_state != 16, d_conv != 4, unknown dtype, size limits */
   AXON_ERR_WORKSPACE_TOO_SMALL = 3,
   AXON_ERR_HIP = 4                /* a HIP launch or runtime call failed */
 } axon_status;

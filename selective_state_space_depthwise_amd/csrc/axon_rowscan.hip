@@ -234,29 +234,44 @@ __device__ __forceinline__ float rows_reduce4(float p0, float p1, float p2, floa
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// Inputs of one tile for this lane, loaded ahead of use. The lane's prologue tokens are
-// ts + 4k + q for k = w*TPL .. w*TPL + TPL - 1; B / C registers as for scan_tile_from.
-template <int SPL, int TPL, int kTile>
+// Inputs of one tile for this lane, loaded ahead of use. The lane's prologue / epilogue tokens
+// are TPL consecutive ones, tau0 .. tau0 + TPL - 1 with tau0 = (4 w + q) TPL, so its conv window
+// is TPL + 3 inputs. B / C registers are laid out as scan_tile_from reads them.
+template <int TPL, int NR>
 struct TileIn {
-  static constexpr int NR = kTile * SPL / 16;  // B (and C) registers per tile
-  float xw[TPL][4];  // x at t-3 .. t for each prologue token t
+  float xw[TPL + 3];  // x at tau0 - 3 .. tau0 + TPL - 1
   float dr[TPL];
   float zz[TPL];
   float RB[NR], RC[NR];
 };
+
+template <typename T>
+__device__ __forceinline__ const T* byte_offset(const T* base, uint32_t off) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
+}
+template <typename T>
+__device__ __forceinline__ T* byte_offset(T* base, uint32_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
+}
 
 template <typename Act, int W, bool kCarry>
 __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
   constexpr int SPL = 4 / W;  // states per lane
   constexpr int kTile = tile_tokens<W>();
   constexpr int kDtStride = 2 * kTile + 4;  // floats per channel in the dt / dtu tile (padded)
-  constexpr int TPL = kTile / (4 * W);  // prologue / epilogue tokens per lane per tile
+  constexpr int TPL = kTile / (4 * W);      // prologue / epilogue tokens per lane per tile
   constexpr int NW = W * kGroups;
   constexpr int TPR = 16 / SPL;         // tokens per B / C register
   constexpr int NR = kTile * SPL / 16;  // B / C registers per tile
-  constexpr int NX = kTile / 16;        // float4 groups of reduced outputs per lane
+  constexpr int NX = kTile / 16;        // groups of 16 readout products reduced together
+  // Reduced outputs: token tau of channel c at tau * 16 + c + 16 * (tau / TPL): the gap of 16
+  // floats after every group of TPL tokens puts the 4 lane rows of the epilogue (which read
+  // tokens TPL apart) on distinct LDS banks.
+  constexpr int kExStride = kTile * 16 + 16 * (kTile / TPL);
+  static_assert(TPL >= 2 && TPL % 2 == 0, "prologue writes token pairs");
   __shared__ __attribute__((aligned(16))) float s_dt[2][kGroups * 16][kDtStride];
-  __shared__ float4 s_ex[2][NW][NX][64];
+  __shared__ float s_ex[2][NW][kExStride];
+  constexpr size_t kElt = sizeof(Act);
 
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -268,8 +283,10 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
   const int64_t b = blockIdx.y;
   const int64_t e_raw = static_cast<int64_t>(blockIdx.x) * (kGroups * 16) + slot;
   const bool valid = e_raw < a.E;
+  const bool block_full = (static_cast<int64_t>(blockIdx.x) + 1) * (kGroups * 16) <= a.E;
   const int64_t e = valid ? e_raw : a.E - 1;
   const int g = w * 4 + q;  // this lane's state group: states g*SPL .. g*SPL + SPL - 1
+  const int tau0 = g * TPL;  // first of this lane's prologue / epilogue tokens in a tile
   const int64_t chunk = blockIdx.z;
   const int64_t tb = chunk * a.T;
   const int64_t te = (tb + a.T < a.L) ? tb + a.T : a.L;
@@ -280,6 +297,19 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
   const Act* __restrict__ dtrp = static_cast<const Act*>(a.dt_raw);
   const Act* __restrict__ Bp = static_cast<const Act*>(a.Bm) + b * L * kState;
   const Act* __restrict__ Cp = static_cast<const Act*>(a.Cm) + b * L * kState;
+  Act* __restrict__ yp = static_cast<Act*>(a.y);
+
+  // Byte offsets of this lane's elements relative to a tile's first token (32-bit; the host
+  // bounds d_inner so that (kTile + 3) * d_inner elements fit).
+  const uint32_t E32 = static_cast<uint32_t>(E);
+  uint32_t xoff[TPL + 3];  // token tau0 + j of channel e (x taps from a base 3 tokens back)
+#pragma unroll
+  for (int j = 0; j < TPL + 3; ++j)
+    xoff[j] = (static_cast<uint32_t>(tau0 + j) * E32 + static_cast<uint32_t>(e)) * kElt;
+  uint32_t bcoff[NR];  // B / C element (token j*TPR + c/SPL, state g*SPL + c%SPL)
+#pragma unroll
+  for (int j = 0; j < NR; ++j)
+    bcoff[j] = static_cast<uint32_t>((j * TPR + c / SPL) * kState + g * SPL + (c % SPL)) * kElt;
 
   float rate[SPL], h[SPL];
 #pragma unroll
@@ -307,39 +337,38 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
     if (tt < 0) return a.win_src ? a.win_src[(b * kHalo + (tt + kHalo)) * E + e] : 0.0f;
     return load_act(xp, (b * L + (tt < L ? tt : L - 1)) * E + e);
   };
-  // This lane's elements of the (b, e) channel: token t at [t * E].
-  const Act* __restrict__ xl = xp + b * L * E + e;
-  const Act* __restrict__ dl = dtrp + b * L * E + e;
-  const Act* __restrict__ zl = zp + b * L * E + e;
-  auto load_tile = [&](int64_t ts, TileIn<SPL, TPL, kTile>& in) {
+  auto load_tile = [&](int64_t ts, TileIn<TPL, NR>& in) {
+    const Act* bc_b = Bp + ts * kState;
+    const Act* bc_c = Cp + ts * kState;
     if (ts >= 3 && ts + kTile <= L) {
-      // Fast path (uniform branch): the tile and its conv halo lie inside the sequence.
+      // Fast path (uniform branch): the tile and its conv halo lie inside the sequence. Every
+      // address is a wave-uniform tile base plus a fixed 32-bit lane offset.
+      const Act* xb = xp + (b * L + ts - 3) * E;
+      const Act* db = dtrp + (b * L + ts) * E;
+      const Act* zb = zp + (b * L + ts) * E;
+#pragma unroll
+      for (int j = 0; j < TPL + 3; ++j) in.xw[j] = load_act(byte_offset(xb, xoff[j]), 0);
 #pragma unroll
       for (int r = 0; r < TPL; ++r) {
-        const int64_t t = ts + 4 * (w * TPL + r) + q;
-        const Act* px = xl + (t - 3) * E;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) in.xw[r][k] = load_act(px, k * E);
-        in.dr[r] = load_act(dl, t * E);
-        if constexpr (!kCarry) in.zz[r] = load_act(zl, t * E);
+        in.dr[r] = load_act(byte_offset(db, xoff[r]), 0);
+        if constexpr (!kCarry) in.zz[r] = load_act(byte_offset(zb, xoff[r]), 0);
       }
 #pragma unroll
       for (int j = 0; j < NR; ++j) {
-        const int64_t tt = ts + j * TPR + c / SPL;
-        const int n = g * SPL + (c % SPL);
-        in.RB[j] = load_act(Bp, tt * kState + n);
-        if constexpr (!kCarry) in.RC[j] = load_act(Cp, tt * kState + n);
+        in.RB[j] = load_act(byte_offset(bc_b, bcoff[j]), 0);
+        if constexpr (!kCarry) in.RC[j] = load_act(byte_offset(bc_c, bcoff[j]), 0);
       }
       return;
     }
+    // Edge tiles: conv halo from the incoming window, tokens past the end clamped.
+    const int64_t t0 = ts + tau0;
+#pragma unroll
+    for (int j = 0; j < TPL + 3; ++j) in.xw[j] = load_x(t0 - 3 + j);
 #pragma unroll
     for (int r = 0; r < TPL; ++r) {
-      const int64_t t = ts + 4 * (w * TPL + r) + q;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) in.xw[r][k] = load_x(t - 3 + k);
-      const int64_t tt = t < L ? t : L - 1;
-      in.dr[r] = load_act(dl, tt * E);
-      if constexpr (!kCarry) in.zz[r] = load_act(zl, tt * E);
+      const int64_t tt = t0 + r < L ? t0 + r : L - 1;
+      in.dr[r] = load_act(dtrp, (b * L + tt) * E + e);
+      if constexpr (!kCarry) in.zz[r] = load_act(zp, (b * L + tt) * E + e);
     }
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
@@ -351,23 +380,30 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
     }
   };
   // dt and dt*u of this lane's prologue tokens into the LDS tile; u is kept for the skip term.
-  auto prologue = [&](int64_t ts, const TileIn<SPL, TPL, kTile>& in, int buf, float (&u)[TPL]) {
+  auto prologue = [&](int64_t ts, const TileIn<TPL, NR>& in, int buf, float (&u)[TPL]) {
+    const bool tile_full = ts + kTile <= te;
+    float pair[2 * TPL];
 #pragma unroll
     for (int r = 0; r < TPL; ++r) {
-      const int tau = 4 * (w * TPL + r) + q;
-      const float uu = fmaf(w3, in.xw[r][3],
-                            fmaf(w2, in.xw[r][2], fmaf(w1, in.xw[r][1], fmaf(w0, in.xw[r][0], cb))));
-      const bool ok = valid && (ts + tau < te);
+      const float uu = fmaf(w3, in.xw[r + 3],
+                            fmaf(w2, in.xw[r + 2], fmaf(w1, in.xw[r + 1], fmaf(w0, in.xw[r], cb))));
+      const bool ok = valid && (tile_full || ts + tau0 + r < te);
       const float dt = ok ? step_size(in.dr[r] + dtb, a.dt_min, a.dt_max) : 0.0f;
-      *reinterpret_cast<float2*>(&s_dt[buf][slot][2 * tau]) = make_float2(dt, dt * uu);
+      pair[2 * r] = dt;
+      pair[2 * r + 1] = dt * uu;
       u[r] = uu;
     }
+#pragma unroll
+    for (int r = 0; r < TPL; r += 2)
+      *reinterpret_cast<float4*>(&s_dt[buf][slot][2 * (tau0 + r)]) =
+          make_float4(pair[2 * r], pair[2 * r + 1], pair[2 * r + 2], pair[2 * r + 3]);
   };
+  auto ex_index = [&](int tau) { return tau * 16 + c + 16 * (tau / TPL); };
 
   const int64_t ntiles = (te - tb + kTile - 1) / kTile;
   // Two static ring slots (a dynamically indexed register array would live in scratch memory):
   // the loop body handles tiles in pairs with the slots' roles swapped.
-  TileIn<SPL, TPL, kTile> ring0, ring1;
+  TileIn<TPL, NR> ring0, ring1;
   float u_cur[TPL], z_cur[TPL], rb[NR], rc[NR];
   load_tile(tb, ring0);
   if (ntiles > 1) load_tile(tb + kTile, ring1);
@@ -382,10 +418,9 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
   __syncthreads();
 
   float S = 0.0f;
-  Act* __restrict__ yp = static_cast<Act*>(a.y);
   // Tile k: its inputs came from `mine`, which then receives tile k+2; tile k+1 (loaded one tile
   // ago into `other`) gets its prologue after the scan of tile k.
-  auto do_tile = [&](int64_t k, TileIn<SPL, TPL, kTile>& mine, const TileIn<SPL, TPL, kTile>& other) {
+  auto do_tile = [&](int64_t k, TileIn<TPL, NR>& mine, const TileIn<TPL, NR>& other) {
     const int64_t ts = tb + k * kTile;
     const int buf = static_cast<int>(k & 1);
     if (k + 2 < ntiles) load_tile(ts + 2 * kTile, mine);
@@ -400,33 +435,27 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
     float u_next[TPL];
     if (has_next) prologue(ts + kTile, other, buf ^ 1, u_next);
     if constexpr (!kCarry) {
+      // Row q of the reduced register for tokens 4x .. 4x+3 holds token 4x + q.
 #pragma unroll
-      for (int x4 = 0; x4 < NX; ++x4) {
-        const float* p = P + 16 * x4;
-        float4 R;
-        R.x = rows_reduce4(p[0], p[1], p[2], p[3]);
-        R.y = rows_reduce4(p[4], p[5], p[6], p[7]);
-        R.z = rows_reduce4(p[8], p[9], p[10], p[11]);
-        R.w = rows_reduce4(p[12], p[13], p[14], p[15]);
-        s_ex[buf][wid][x4][lane] = R;
+      for (int x4 = 0; x4 < 4 * NX; ++x4) {
+        const float R = rows_reduce4(P[4 * x4], P[4 * x4 + 1], P[4 * x4 + 2], P[4 * x4 + 3]);
+        s_ex[buf][wid][ex_index(4 * x4 + q)] = R;
       }
     }
     __syncthreads();
     if constexpr (!kCarry) {
-      // This wave finishes tokens ts + 4k + q, k = w*TPL .. w*TPL + TPL - 1, of channel e: the
-      // tokens its prologue computed.
+      // This wave finishes its prologue tokens: skip term, gate, store.
+      Act* yt = yp + (b * L + ts) * E;
+      const bool store_all = block_full && ts + kTile <= te;
 #pragma unroll
       for (int r = 0; r < TPL; ++r) {
-        const int kk = w * TPL + r;
-        float ysum = 0.0f;
+        const int ix = ex_index(tau0 + r);
+        float ysum = s_ex[buf][grp * W][ix];
 #pragma unroll
-        for (int v = 0; v < W; ++v)
-          ysum += reinterpret_cast<const float*>(&s_ex[buf][grp * W + v][kk >> 2][lane])[kk & 3];
-        const int64_t t = ts + 4 * kk + q;
-        if (valid && t < te) {
-          const float yv = fmaf(Dv, u_cur[r], ysum) * silu(z_cur[r]);
-          store_act(yp, (b * L + t) * E + e, yv);
-        }
+        for (int v = 1; v < W; ++v) ysum += s_ex[buf][grp * W + v][ix];
+        const float yv = fmaf(Dv, u_cur[r], ysum) * silu(z_cur[r]);
+        if (store_all || (valid && ts + tau0 + r < te))
+          store_act(byte_offset(yt, xoff[r]), 0, yv);
       }
     }
     if (has_next) {

@@ -13,6 +13,9 @@ namespace {
 constexpr int kVersion = 100;  // 0.1.0
 constexpr int64_t kMaxBatch = 65535;      // launch grid y dimension
 constexpr int64_t kMaxElems = int64_t(1) << 40;
+// The prefill kernels address a tile of (32 + 3) tokens x d_inner channels with 32-bit byte
+// offsets.
+constexpr int64_t kMaxDInner = int64_t(1) << 24;
 
 // The prefill wants about one wave per SIMD (256 CUs x 4 SIMDs x 64 lanes = 65536). Below half of
 // that many (channel, state-group) lanes it also cuts the sequence into chunks of at least
@@ -57,7 +60,7 @@ axon_status check_shape(const axon_ssm_shape* s, bool prefill) {
   if (s->act_dtype != AXON_F32 && s->act_dtype != AXON_BF16) return AXON_ERR_UNSUPPORTED;
   if (s->batch < 1 || s->d_inner < 1 || (prefill && s->seqlen < 0))
     return AXON_ERR_INVALID_ARGUMENT;
-  if (s->batch > kMaxBatch) return AXON_ERR_UNSUPPORTED;
+  if (s->batch > kMaxBatch || s->d_inner > kMaxDInner) return AXON_ERR_UNSUPPORTED;
   int64_t t = 0;
   const int64_t L = prefill ? s->seqlen : 1;
   if (!mul_ok(s->batch, L, &t) || !mul_ok(t, s->d_inner, &t) || !mul_ok(t, axon::kState, &t))
