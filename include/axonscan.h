@@ -39,7 +39,7 @@
  *
  * Supported shapes: d_state == 16, d_conv == 4 (the layer configuration table of [AXON]);
  * batch >= 1, d_inner >= 1, seqlen >= 0 (else AXON_ERR_INVALID_ARGUMENT);
- * batch <= 65535 and d_inner <= 2^24 (else AXON_ERR_UNSUPPORTED);
+ * batch <= 65535 and d_inner <= 2^23 (else AXON_ERR_UNSUPPORTED);
  * batch*seqlen*d_inner*d_state <= 2^40 (else AXON_ERR_INVALID_ARGUMENT).
  * Activation dtype: fp32 or bf16 (bf16 outputs are rounded to nearest even from fp32).
  * State, cache and parameters are always fp32; the state recurrence runs in fp32.

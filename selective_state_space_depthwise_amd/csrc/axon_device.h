@@ -44,6 +44,46 @@ __device__ __forceinline__ void store_act(bf16_bits* p, int64_t i, float v) {
   p[i] = static_cast<bf16_bits>(u >> 16);
 }
 
+// Raw buffer access: a wave-uniform 128-bit resource (base address in SGPRs) plus a 32-bit
+// per-lane byte offset. Stride 0 and num_records 0xFFFFFFFF make every 32-bit offset in range;
+// the data-format field is set to 32 bit only because a zero format marks the resource invalid.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
+}
+// A resource whose range is the first `bytes` bytes at base: an access at a byte offset at or
+// past the range is out of range, so a load returns 0 and a store is dropped by the hardware.
+// Stores use it to mask lanes without a branch (offset kNoStore, or past the valid range).
+constexpr uint32_t kNoStore = 0x80000000u;
+__device__ __forceinline__ rsrc_t make_rsrc_bounded(void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
+}
+
+template <typename Act>
+__device__ __forceinline__ float load_buf(rsrc_t r, uint32_t off);
+template <>
+__device__ __forceinline__ float load_buf<float>(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+template <>
+__device__ __forceinline__ float load_buf<bf16_bits>(rsrc_t r, uint32_t off) {
+  return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+
+template <typename Act>
+__device__ __forceinline__ void store_buf(rsrc_t r, uint32_t off, float v);
+template <>
+__device__ __forceinline__ void store_buf<float>(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+template <>
+__device__ __forceinline__ void store_buf<bf16_bits>(rsrc_t r, uint32_t off, float v) {
+  uint32_t u = __float_as_uint(v);  // round to nearest, ties to even
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(u >> 16), r, off, 0, 0);
+}
+
 // A_n * log2(e) with A_n = -exp(A_log_n), so that exp(dt A_n) = exp2(dt * rate).
 __device__ __forceinline__ float decay_rate_log2(float a_log) { return -expf(a_log) * kLog2e; }
 

@@ -29,6 +29,8 @@
 // one instruction later. A token's readout products are computed one block late, so the state they
 // read is old enough for DPP; the products of a tile's last token are taken after an s_nop 1, and
 // that block ends with an s_nop 1 before any instruction the compiler places after it.
+#include <type_traits>
+
 #include "axon_device.h"
 #include "axon_internal.h"
 
@@ -245,15 +247,6 @@ struct TileIn {
   float RB[NR], RC[NR];
 };
 
-template <typename T>
-__device__ __forceinline__ const T* byte_offset(const T* base, uint32_t off) {
-  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
-}
-template <typename T>
-__device__ __forceinline__ T* byte_offset(T* base, uint32_t off) {
-  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
-}
-
 template <typename Act, int W, bool kCarry>
 __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
   constexpr int SPL = 4 / W;  // states per lane
@@ -283,7 +276,6 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
   const int64_t b = blockIdx.y;
   const int64_t e_raw = static_cast<int64_t>(blockIdx.x) * (kGroups * 16) + slot;
   const bool valid = e_raw < a.E;
-  const bool block_full = (static_cast<int64_t>(blockIdx.x) + 1) * (kGroups * 16) <= a.E;
   const int64_t e = valid ? e_raw : a.E - 1;
   const int g = w * 4 + q;  // this lane's state group: states g*SPL .. g*SPL + SPL - 1
   const int tau0 = g * TPL;  // first of this lane's prologue / epilogue tokens in a tile
@@ -299,13 +291,22 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
   const Act* __restrict__ Cp = static_cast<const Act*>(a.Cm) + b * L * kState;
   Act* __restrict__ yp = static_cast<Act*>(a.y);
 
-  // Byte offsets of this lane's elements relative to a tile's first token (32-bit; the host
-  // bounds d_inner so that (kTile + 3) * d_inner elements fit).
+  // Byte offsets of this lane's elements (the host bounds d_inner so that (kTile + 3) * d_inner
+  // elements stay below 2^31 bytes): xoff[j] is token tau0 + j of channel e relative to a
+  // tile-aligned base, used for x with the base 3 tokens before the tile (x taps tau0 - 3 + j)
+  // and, for j < TPL, for dt_raw and z with the base at the tile's first token. yoff is the
+  // same for y, or kNoStore for a lane past the last channel.
   const uint32_t E32 = static_cast<uint32_t>(E);
   uint32_t xoff[TPL + 3];  // token tau0 + j of channel e (x taps from a base 3 tokens back)
 #pragma unroll
   for (int j = 0; j < TPL + 3; ++j)
     xoff[j] = (static_cast<uint32_t>(tau0 + j) * E32 + static_cast<uint32_t>(e)) * kElt;
+  uint32_t xoff_t[TPL], yoff[TPL];
+#pragma unroll
+  for (int r = 0; r < TPL; ++r) {
+    xoff_t[r] = xoff[r];
+    yoff[r] = valid ? xoff[r] : kNoStore;
+  }
   uint32_t bcoff[NR];  // B / C element (token j*TPR + c/SPL, state g*SPL + c%SPL)
 #pragma unroll
   for (int j = 0; j < NR; ++j)
@@ -337,30 +338,8 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
     if (tt < 0) return a.win_src ? a.win_src[(b * kHalo + (tt + kHalo)) * E + e] : 0.0f;
     return load_act(xp, (b * L + (tt < L ? tt : L - 1)) * E + e);
   };
-  auto load_tile = [&](int64_t ts, TileIn<TPL, NR>& in) {
-    const Act* bc_b = Bp + ts * kState;
-    const Act* bc_c = Cp + ts * kState;
-    if (ts >= 3 && ts + kTile <= L) {
-      // Fast path (uniform branch): the tile and its conv halo lie inside the sequence. Every
-      // address is a wave-uniform tile base plus a fixed 32-bit lane offset.
-      const Act* xb = xp + (b * L + ts - 3) * E;
-      const Act* db = dtrp + (b * L + ts) * E;
-      const Act* zb = zp + (b * L + ts) * E;
-#pragma unroll
-      for (int j = 0; j < TPL + 3; ++j) in.xw[j] = load_act(byte_offset(xb, xoff[j]), 0);
-#pragma unroll
-      for (int r = 0; r < TPL; ++r) {
-        in.dr[r] = load_act(byte_offset(db, xoff[r]), 0);
-        if constexpr (!kCarry) in.zz[r] = load_act(byte_offset(zb, xoff[r]), 0);
-      }
-#pragma unroll
-      for (int j = 0; j < NR; ++j) {
-        in.RB[j] = load_act(byte_offset(bc_b, bcoff[j]), 0);
-        if constexpr (!kCarry) in.RC[j] = load_act(byte_offset(bc_c, bcoff[j]), 0);
-      }
-      return;
-    }
-    // Edge tiles: conv halo from the incoming window, tokens past the end clamped.
+  // The first two tiles: conv halo from the incoming window, tokens past the end clamped.
+  auto load_tile_first = [&](int64_t ts, TileIn<TPL, NR>& in) {
     const int64_t t0 = ts + tau0;
 #pragma unroll
     for (int j = 0; j < TPL + 3; ++j) in.xw[j] = load_x(t0 - 3 + j);
@@ -379,16 +358,62 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
       if constexpr (!kCarry) in.RC[j] = load_act(Cp, tt * kState + n);
     }
   };
-  // dt and dt*u of this lane's prologue tokens into the LDS tile; u is kept for the skip term.
+  // Tiles loaded inside the loop start at ts >= tb + 2 kTile >= 3, so their conv halo is in x,
+  // and at ts <= L - 1. Addresses are a wave-uniform buffer resource per tile plus 32-bit lane
+  // offsets; a tile that runs past the end of the sequence clamps its tokens to L - 1 through
+  // its offsets. Both cases issue the same loads into the same registers with no per-lane
+  // branch, so the compiler's wait counts stay exact.
+  auto load_seq = [&](int64_t ts, TileIn<TPL, NR>& in, const uint32_t (&xo)[TPL + 3],
+                      const uint32_t (&to)[TPL], const uint32_t (&bo)[NR]) {
+    const rsrc_t rx = make_rsrc(xp + (b * L + ts - 3) * E);
+    const rsrc_t rd = make_rsrc(dtrp + (b * L + ts) * E);
+    const rsrc_t rz = make_rsrc(zp + (b * L + ts) * E);
+    const rsrc_t rB = make_rsrc(Bp + ts * kState);
+    const rsrc_t rC = make_rsrc(Cp + ts * kState);
+#pragma unroll
+    for (int j = 0; j < TPL + 3; ++j) in.xw[j] = load_buf<Act>(rx, xo[j]);
+#pragma unroll
+    for (int r = 0; r < TPL; ++r) {
+      in.dr[r] = load_buf<Act>(rd, to[r]);
+      if constexpr (!kCarry) in.zz[r] = load_buf<Act>(rz, to[r]);
+    }
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      in.RB[j] = load_buf<Act>(rB, bo[j]);
+      if constexpr (!kCarry) in.RC[j] = load_buf<Act>(rC, bo[j]);
+    }
+  };
+  auto load_tile = [&](int64_t ts, TileIn<TPL, NR>& in) {
+    if (ts + kTile <= L) {
+      load_seq(ts, in, xoff, xoff_t, bcoff);
+    } else {
+      const int lim = static_cast<int>(L - 1 - ts);  // last token of the sequence, tile-relative
+      const uint32_t e32 = static_cast<uint32_t>(e);
+      uint32_t xo[TPL + 3], to[TPL], bo[NR];
+#pragma unroll
+      for (int j = 0; j < TPL + 3; ++j)
+        xo[j] = (static_cast<uint32_t>(min(tau0 + j - 3, lim) + 3) * E32 + e32) * kElt;
+#pragma unroll
+      for (int r = 0; r < TPL; ++r)
+        to[r] = (static_cast<uint32_t>(min(tau0 + r, lim)) * E32 + e32) * kElt;
+#pragma unroll
+      for (int j = 0; j < NR; ++j)
+        bo[j] = static_cast<uint32_t>(min(j * TPR + c / SPL, lim) * kState + g * SPL + (c % SPL)) *
+                kElt;
+      load_seq(ts, in, xo, to, bo);
+    }
+  };
+  // Tokens past the chunk end (and lanes past the last channel) get dt = 0: their state update
+  // is the identity.
   auto prologue = [&](int64_t ts, const TileIn<TPL, NR>& in, int buf, float (&u)[TPL]) {
-    const bool tile_full = ts + kTile <= te;
+    const int rem = static_cast<int>(te - ts < kTile ? te - ts : kTile);  // tokens in the chunk
     float pair[2 * TPL];
 #pragma unroll
     for (int r = 0; r < TPL; ++r) {
       const float uu = fmaf(w3, in.xw[r + 3],
                             fmaf(w2, in.xw[r + 2], fmaf(w1, in.xw[r + 1], fmaf(w0, in.xw[r], cb))));
-      const bool ok = valid && (tile_full || ts + tau0 + r < te);
-      const float dt = ok ? step_size(in.dr[r] + dtb, a.dt_min, a.dt_max) : 0.0f;
+      const float keep = (valid && tau0 + r < rem) ? 1.0f : 0.0f;
+      const float dt = step_size(in.dr[r] + dtb, a.dt_min, a.dt_max) * keep;
       pair[2 * r] = dt;
       pair[2 * r + 1] = dt * uu;
       u[r] = uu;
@@ -401,39 +426,36 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
   auto ex_index = [&](int tau) { return tau * 16 + c + 16 * (tau / TPL); };
 
   const int64_t ntiles = (te - tb + kTile - 1) / kTile;
-  // Two static ring slots (a dynamically indexed register array would live in scratch memory):
-  // the loop body handles tiles in pairs with the slots' roles swapped.
-  TileIn<TPL, NR> ring0, ring1;
-  float u_cur[TPL], z_cur[TPL], rb[NR], rc[NR];
-  load_tile(tb, ring0);
-  if (ntiles > 1) load_tile(tb + kTile, ring1);
+  const int64_t ts_last = tb + (ntiles - 1) * kTile;
+  // Three register slots (a dynamically indexed register array would live in scratch memory):
+  // while tile k is scanned, tile k+1's inputs wait for their prologue and tile k+2's are in
+  // flight. The main loop handles whole triples of tiles with the slots' roles rotated, so
+  // loaded registers are never copied (a copy would wait for its load).
+  TileIn<TPL, NR> ring0, ring1, ring2;
+  float u_cur[TPL];
+  load_tile_first(tb, ring0);
+  if (ntiles > 1) load_tile_first(tb + kTile, ring1);
   prologue(tb, ring0, 0, u_cur);
-#pragma unroll
-  for (int r = 0; r < TPL; ++r) z_cur[r] = ring0.zz[r];
-#pragma unroll
-  for (int j = 0; j < NR; ++j) {
-    rb[j] = ring0.RB[j];
-    rc[j] = ring0.RC[j];
-  }
   __syncthreads();
 
   float S = 0.0f;
-  // Tile k: its inputs came from `mine`, which then receives tile k+2; tile k+1 (loaded one tile
-  // ago into `other`) gets its prologue after the scan of tile k.
-  auto do_tile = [&](int64_t k, TileIn<TPL, NR>& mine, const TileIn<TPL, NR>& other) {
+  // Tile k: scan with cur's B / C, prologue of tile k+1 from nxt, epilogue with cur's z; with
+  // kLoad, tile k+2 (clamped to the last tile) is first loaded into fut.
+  auto do_tile = [&](auto load_tag, int64_t k, const TileIn<TPL, NR>& cur,
+                     const TileIn<TPL, NR>& nxt, TileIn<TPL, NR>& fut) {
+    constexpr bool kLoad = decltype(load_tag)::value;
     const int64_t ts = tb + k * kTile;
     const int buf = static_cast<int>(k & 1);
-    if (k + 2 < ntiles) load_tile(ts + 2 * kTile, mine);
+    if constexpr (kLoad) load_tile(ts + 2 * kTile < ts_last ? ts + 2 * kTile : ts_last, fut);
     float4 dd[kTile / 2];
 #pragma unroll
     for (int i = 0; i < kTile / 2; ++i)
       dd[i] = *reinterpret_cast<const float4*>(&s_dt[buf][slot][4 * i]);
     float P[kTile], ac[SPL];
-    scan_tile_from<SPL, kCarry, 0, kTile>(dd, rate, rb, rc, h, ac, P, S);
+    scan_tile_from<SPL, kCarry, 0, kTile>(dd, rate, cur.RB, cur.RC, h, ac, P, S);
 
-    const bool has_next = k + 1 < ntiles;
     float u_next[TPL];
-    if (has_next) prologue(ts + kTile, other, buf ^ 1, u_next);
+    if (k + 1 < ntiles) prologue(ts + kTile, nxt, buf ^ 1, u_next);
     if constexpr (!kCarry) {
       // Row q of the reduced register for tokens 4x .. 4x+3 holds token 4x + q.
 #pragma unroll
@@ -444,37 +466,37 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
     }
     __syncthreads();
     if constexpr (!kCarry) {
-      // This wave finishes its prologue tokens: skip term, gate, store.
-      Act* yt = yp + (b * L + ts) * E;
-      const bool store_all = block_full && ts + kTile <= te;
+      // This wave finishes its prologue tokens: skip term, gate, store. Every lane issues its
+      // stores; those of tokens past the chunk end fall outside the resource's range and those
+      // of lanes past the last channel carry kNoStore, so the hardware drops them and no
+      // branch is needed.
+      const int64_t rem = te - ts < kTile ? te - ts : kTile;
+      const rsrc_t ry = make_rsrc_bounded(yp + (b * L + ts) * E,
+                                          static_cast<uint32_t>(rem * E * kElt));
 #pragma unroll
       for (int r = 0; r < TPL; ++r) {
         const int ix = ex_index(tau0 + r);
         float ysum = s_ex[buf][grp * W][ix];
 #pragma unroll
         for (int v = 1; v < W; ++v) ysum += s_ex[buf][grp * W + v][ix];
-        const float yv = fmaf(Dv, u_cur[r], ysum) * silu(z_cur[r]);
-        if (store_all || (valid && ts + tau0 + r < te))
-          store_act(byte_offset(yt, xoff[r]), 0, yv);
+        const float yv = fmaf(Dv, u_cur[r], ysum) * silu(cur.zz[r]);
+        store_buf<Act>(ry, yoff[r], yv);
       }
     }
-    if (has_next) {
 #pragma unroll
-      for (int r = 0; r < TPL; ++r) {
-        u_cur[r] = u_next[r];
-        z_cur[r] = other.zz[r];
-      }
-#pragma unroll
-      for (int j = 0; j < NR; ++j) {
-        rb[j] = other.RB[j];
-        rc[j] = other.RC[j];
-      }
-    }
+    for (int r = 0; r < TPL; ++r) u_cur[r] = u_next[r];
   };
-  for (int64_t k = 0; k < ntiles; k += 2) {
-    do_tile(k, ring0, ring1);
-    if (k + 1 < ntiles) do_tile(k + 1, ring1, ring0);
+  using Load = std::true_type;
+  using NoLoad = std::false_type;
+  int64_t k = 0;
+  for (; k + 3 <= ntiles; k += 3) {
+    do_tile(Load{}, k, ring0, ring1, ring2);
+    do_tile(Load{}, k + 1, ring1, ring2, ring0);
+    do_tile(Load{}, k + 2, ring2, ring0, ring1);
   }
+  // At most two tiles remain, whose inputs are already loaded (in ring0 and ring1).
+  if (k < ntiles) do_tile(NoLoad{}, k, ring0, ring1, ring2);
+  if (k + 1 < ntiles) do_tile(NoLoad{}, k + 1, ring1, ring2, ring0);
 
   if (!valid) return;
   if constexpr (kCarry) {

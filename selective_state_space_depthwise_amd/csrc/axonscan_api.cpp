@@ -13,9 +13,9 @@ namespace {
 constexpr int kVersion = 100;  // 0.1.0
 constexpr int64_t kMaxBatch = 65535;      // launch grid y dimension
 constexpr int64_t kMaxElems = int64_t(1) << 40;
-// The prefill kernels address a tile of (32 + 3) tokens x d_inner channels with 32-bit byte
-// offsets.
-constexpr int64_t kMaxDInner = int64_t(1) << 24;
+// The prefill kernels address a tile of (32 + 3) tokens x d_inner channels with byte offsets
+// below 2^31 (offset 2^31 marks a masked store).
+constexpr int64_t kMaxDInner = int64_t(1) << 23;
 
 // The prefill wants about one wave per SIMD (256 CUs x 4 SIMDs x 64 lanes = 65536). Below half of
 // that many (channel, state-group) lanes it also cuts the sequence into chunks of at least

@@ -82,7 +82,7 @@ def test_workspace_is_a_pure_function_of_shape():
 @pytest.mark.parametrize("kw,status", [
     (dict(d_state=8), A.AXON_ERR_UNSUPPORTED),
     (dict(d_state=32), A.AXON_ERR_UNSUPPORTED),
-    (dict(d_inner=(1 << 24) + 1, seqlen=1), A.AXON_ERR_UNSUPPORTED),
+    (dict(d_inner=(1 << 23) + 1, seqlen=1), A.AXON_ERR_UNSUPPORTED),
     (dict(batch=65536, d_inner=1, seqlen=1), A.AXON_ERR_UNSUPPORTED),
     (dict(d_conv=3), A.AXON_ERR_UNSUPPORTED),
     (dict(batch=0), A.AXON_ERR_INVALID_ARGUMENT),
