@@ -27,6 +27,7 @@ import workloads  # noqa: E402
 METRIC = "selective-scan tokens/s at E=7680,N=16,L=2048 + % of HBM peak GB/s"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
 N_STATE, K_CONV = 16, 4
+COPY_BYTES = 512 << 20  # calibration copy: 512 MiB read + 512 MiB written per dispatch
 
 
 def algorithmic_bytes(Bsz, L, E, elt, with_cache_in=False, with_state_in=False):
@@ -38,6 +39,32 @@ def algorithmic_bytes(Bsz, L, E, elt, with_cache_in=False, with_state_in=False):
     inn = (4 * Bsz * (K_CONV - 1) * E if with_cache_in else 0) + \
         (4 * Bsz * E * N_STATE if with_state_in else 0)
     return act + prm + out + inn
+
+
+def decode_algorithmic_bytes(Bsz, E, elt):
+    """Bytes one decode step must move: x, z, dt_raw read and y written (B, E); B, C (B, N);
+    the conv cache and the state read and written in place (fp32); parameters read once."""
+    act = 4 * Bsz * E * elt + 2 * Bsz * N_STATE * elt
+    caches = 2 * 4 * (Bsz * (K_CONV - 1) * E + Bsz * E * N_STATE)
+    prm = 4 * (E * N_STATE + 3 * E + E * K_CONV)
+    return act + caches + prm
+
+
+def calibrate_copy(steps):
+    """A plain device-to-device copy of a known size, for scaling rocprofv3's FETCH_SIZE and
+    WRITE_SIZE counters (KiB per dispatch) into bytes: each dispatch reads and writes
+    COPY_BYTES."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    n = COPY_BYTES // 4
+    src = torch.arange(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_dispatch": COPY_BYTES,
+                      "bytes_written_per_dispatch": COPY_BYTES, "dispatches": steps}), flush=True)
 
 
 def cpu_baseline(inp, min_seconds=10.0):
@@ -71,6 +98,8 @@ def main():
     ap.add_argument("--workload", default="axon_prefill_f32_b1_l2048_e7680")
     ap.add_argument("--rotate", type=int, default=3, help="input sets cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain device copy of known size (counter calibration)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 counters), if present")
     args = ap.parse_args()
@@ -80,13 +109,18 @@ def main():
               "one process per GPU on its own share.", file=sys.stderr)
         sys.exit(2)
 
+    if args.calibrate_copy:
+        calibrate_copy(args.steps)
+        return
+
     import torch
 
     import selective_state_space_depthwise_amd as axon
 
     w = workloads.workload(args.workload)
-    if w.kind != "prefill":
-        sys.exit("bench.py times prefill workloads")
+    if w.kind == "decode":
+        bench_decode(args, w)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     adt = torch.bfloat16 if w.act == "bf16" else torch.float32
@@ -172,6 +206,75 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp0)
+    print(json.dumps(line), flush=True)
+
+
+def bench_decode(args, w):
+    """One step = one axon_ssm_decode_step over the whole batch (one token per sequence); the
+    caches are seeded by a prefill of the workload's prompt length and updated in place."""
+    import torch
+
+    import selective_state_space_depthwise_amd as axon
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    adt = torch.bfloat16 if w.act == "bf16" else torch.float32
+    elt = 2 if w.act == "bf16" else 4
+    Bsz, E = w.batch, w.d_inner
+    inp0 = workloads.prefill_inputs(w)
+    t = {k: torch.from_numpy(inp0[k]).to(dev) for k in ("A_log", "D", "dt_bias", "conv_w",
+                                                       "conv_b")}
+    pre = {k: torch.from_numpy(inp0[k]).to(dev).to(adt) for k in ("x", "z", "dt_raw", "B", "C")}
+    _, cache, state = axon.prefill(pre["x"], pre["z"], pre["dt_raw"], pre["B"], pre["C"],
+                                   t["A_log"], t["D"], t["dt_bias"], t["conv_w"], t["conv_b"],
+                                   dt_min=inp0["dt_min"], dt_max=inp0["dt_max"])
+    nsets = max(1, min(args.rotate * 8, w.decode_steps or 1))
+    steps_in = []
+    for s_ in range(nsets):
+        st = workloads.decode_step_inputs(w, s_)
+        steps_in.append({k: torch.from_numpy(st[k]).to(dev).to(adt) for k in st})
+    y = torch.empty((Bsz, E), dtype=adt, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        st = steps_in[i % nsets]
+        axon.decode_step(st["x"], st["z"], st["dt_raw"], st["B"], st["C"], t["A_log"], t["D"],
+                         t["dt_bias"], t["conv_w"], t["conv_b"], cache, state,
+                         dt_min=inp0["dt_min"], dt_max=inp0["dt_max"], y=y, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(args.warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_per_step = wall * 1e3 / args.steps
+    alg = decode_algorithmic_bytes(Bsz, E, elt)
+    launch_ms = float(ev_ms.mean())
+    achieved = alg / (launch_ms / 1e3) / 1e9
+    line = {
+        "metric": "decode tokens/s (one token per sequence per step)",
+        "value": round(Bsz / (ms_per_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.act,
+        "data": "synthetic (seeded normal draws; caches from a seeded prefill)",
+        "config": {"workload": w.name, "batch": Bsz, "d_inner": E, "d_state": N_STATE,
+                   "d_conv": K_CONV, "prompt_tokens": w.seqlen, "act_dtype": w.act},
+        "event_ms": {"mean": round(launch_ms, 5), "min": round(float(ev_ms.min()), 5),
+                     "median": round(float(np.median(ev_ms)), 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": alg,
+                     "note": "state and cache (B E (N + 3) fp32) stay in the last-level cache "
+                             "between steps"},
+    }
     print(json.dumps(line), flush=True)
 
 
