@@ -580,17 +580,12 @@ int launch_row_scan_t(const PrefillLaunch& p, const PrefillPlan& plan, hipStream
 
 int launch_row_scan(const PrefillLaunch& p, const PrefillPlan& plan, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (plan.row_waves) {
-    case 1:
-      return p.act_bf16 ? launch_row_scan_t<bf16_bits, 1>(p, plan, s)
-                        : launch_row_scan_t<float, 1>(p, plan, s);
-    case 2:
-      return p.act_bf16 ? launch_row_scan_t<bf16_bits, 2>(p, plan, s)
-                        : launch_row_scan_t<float, 2>(p, plan, s);
-    default:
-      return p.act_bf16 ? launch_row_scan_t<bf16_bits, 4>(p, plan, s)
-                        : launch_row_scan_t<float, 4>(p, plan, s);
-  }
+  // The planner picks W = 4 (one state per lane) or W = 2 (two states per lane).
+  if (plan.row_waves == 4)
+    return p.act_bf16 ? launch_row_scan_t<bf16_bits, 4>(p, plan, s)
+                      : launch_row_scan_t<float, 4>(p, plan, s);
+  return p.act_bf16 ? launch_row_scan_t<bf16_bits, 2>(p, plan, s)
+                    : launch_row_scan_t<float, 2>(p, plan, s);
 }
 
 }  // namespace axon

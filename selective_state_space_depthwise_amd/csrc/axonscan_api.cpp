@@ -17,17 +17,19 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;
 // below 2^31 (offset 2^31 marks a masked store).
 constexpr int64_t kMaxDInner = int64_t(1) << 23;
 
-// The prefill wants about one wave per SIMD (256 CUs x 4 SIMDs x 64 lanes = 65536). Below half of
-// that many (channel, state-group) lanes it also cuts the sequence into chunks of at least
-// kMinChunk tokens.
-constexpr int64_t kTargetLanes = 65536;
-constexpr int64_t kChunkBelowLanes = 32768;
+// Work split of the prefill (measured on MI355X, 1024 SIMDs):
+//  - from kSinglePassChannels channels, one state per lane (W = 4 waves per 16 channels) gives
+//    about two waves per SIMD without cutting the sequence: 7680 channels -> 1920 waves;
+//  - from kTwoStateChannels channels, two states per lane (W = 2) is faster (more work per wave,
+//    half the cross-wave traffic): 61440 channels -> 7680 waves;
+//  - below kSinglePassChannels, two states per lane plus time chunks (a carry pass, a combine
+//    and a final pass) up to about kTargetLanes lanes in the final pass (two waves per SIMD),
+//    with chunks of at least kMinChunk tokens.
+constexpr int64_t kSinglePassChannels = 6144;
+constexpr int64_t kTwoStateChannels = 16384;
+constexpr int64_t kTargetLanes = 131072;
 constexpr int64_t kMinChunk = 256;
 constexpr int64_t kMaxChunks = 64;
-// Channel counts from which the scan packs 4 (resp. 2) states per lane: a wave covers 16
-// channels x 16 / W states, and about two waves per SIMD (2048 waves) hide latency.
-constexpr int64_t kRowW1Channels = 32768;
-constexpr int64_t kRowW2Channels = 16384;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -97,12 +99,11 @@ namespace axon {
 PrefillPlan plan_prefill(int64_t batch, int64_t seqlen, int64_t d_inner) {
   PrefillPlan plan;
   const int64_t channels = batch * d_inner;
-  // States per lane 4 / W: as many as the channel count allows while still giving the GPU about
-  // two waves per SIMD.
-  plan.row_waves = channels >= kRowW1Channels ? 1 : (channels >= kRowW2Channels ? 2 : 4);
+  const bool single_pass = channels >= kSinglePassChannels;
+  plan.row_waves = single_pass && channels < kTwoStateChannels ? 4 : 2;
   const int64_t lanes = channels * 4 * plan.row_waves;
   int64_t M = 1;
-  if (lanes < kChunkBelowLanes) {
+  if (!single_pass) {
     M = (kTargetLanes + lanes - 1) / lanes;
     int64_t max_m = seqlen / kMinChunk;
     if (max_m < 1) max_m = 1;
