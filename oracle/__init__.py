@@ -11,6 +11,10 @@ Array conventions (all numpy, C-contiguous):
   A_log: (E, N) float32   D, dt_bias, conv_b: (E,) float32   conv_w: (E, K) float32
   conv_cache: (B, K-1, E) float64   ssm_state: (B, E, N) float64
 Results are float64.
+
+Variants (optional keys of the input / parameter dict): ``conv_activation`` "none" (default,
+Axon-SSM) or "silu" (SiLU on the convolution output, the Mamba block); ``discretization``
+"first_order" (default, Bbar = dt B) or "zoh" (Bbar = expm1(dt A) / A B).
 """
 from __future__ import annotations
 
@@ -47,21 +51,32 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+CONV_ACTIVATIONS = {"none": 0, "silu": 1}
+DISCRETIZATIONS = {"first_order": 0, "zoh": 1}
+
+
+def _variant(d: dict):
+    """(conv_act, disc) codes from the optional variant keys of an input / parameter dict."""
+    return (CONV_ACTIVATIONS[d.get("conv_activation", "none")],
+            DISCRETIZATIONS[d.get("discretization", "first_order")])
+
+
 def _declare(lib):
     P = ctypes.c_void_p
     I = ctypes.c_int64
     Dd = ctypes.c_double
+    Ci = ctypes.c_int
     lib.oracle_ssm_channel.restype = ctypes.c_int
     lib.oracle_ssm_channel.argtypes = [
-        I, I, I, P, P, P, I, P, P, I, P, Dd, Dd, P, Dd, Dd, Dd, P, P, P, I, P, P, P, P, P,
+        I, I, I, P, P, P, I, P, P, I, P, Dd, Dd, P, Dd, Dd, Dd, Ci, Ci, P, P, P, I, P, P, P, P, P,
     ]
     lib.oracle_ssm_prefill.restype = ctypes.c_int
     lib.oracle_ssm_prefill.argtypes = [
-        I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, Dd, Dd, P, P, P, P, P, P, ctypes.c_int,
+        I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, Dd, Dd, Ci, Ci, P, P, P, P, P, P, Ci,
     ]
     lib.oracle_ssm_decode_step.restype = ctypes.c_int
     lib.oracle_ssm_decode_step.argtypes = [
-        I, I, I, I, P, P, P, P, P, P, P, P, P, P, Dd, Dd, P, P, P, ctypes.c_int,
+        I, I, I, I, P, P, P, P, P, P, P, P, P, P, Dd, Dd, Ci, Ci, P, P, P, Ci,
     ]
     return lib
 
@@ -120,8 +135,8 @@ def prefill(inp: dict, conv_cache_in=None, ssm_state_in=None, threads: int = 1,
     mag = np.empty((Bsz, L, E), np.float64) if magnitude else None
     rc = lib.oracle_ssm_prefill(
         Bsz, L, E, N, K, _ptr(x), _ptr(z), _ptr(dtr), _ptr(Bm), _ptr(Cm), _ptr(A_log), _ptr(D),
-        _ptr(dtb), _ptr(w), _ptr(cb), float(inp["dt_min"]), float(inp["dt_max"]), _ptr(cin),
-        _ptr(sin), _ptr(y), _ptr(cout), _ptr(sout), _ptr(mag), int(threads),
+        _ptr(dtb), _ptr(w), _ptr(cb), float(inp["dt_min"]), float(inp["dt_max"]), *_variant(inp),
+        _ptr(cin), _ptr(sin), _ptr(y), _ptr(cout), _ptr(sout), _ptr(mag), int(threads),
     )
     if rc != 0:
         raise ValueError("oracle_ssm_prefill rejected its arguments")
@@ -160,7 +175,8 @@ def channel(inp: dict, b: int, e: int, conv_cache_in=None, ssm_state_in=None, li
     rc = lib.oracle_ssm_channel(
         L, N, K, _ptr(xc), _ptr(zc), _ptr(dc), 1, _ptr(Bc), _ptr(Cc), N, _ptr(A_log[e]),
         float(inp["D"][e]), float(inp["dt_bias"][e]), _ptr(w[e]), float(inp["conv_b"][e]),
-        float(inp["dt_min"]), float(inp["dt_max"]), _ptr(win), _ptr(h0), _ptr(y), 1,
+        float(inp["dt_min"]), float(inp["dt_max"]), *_variant(inp), _ptr(win), _ptr(h0),
+        _ptr(y), 1,
         _ptr(wout), _ptr(hout), _ptr(u), _ptr(dt), _ptr(mag),
     )
     if rc != 0:
@@ -189,7 +205,7 @@ def decode_step(step: dict, params: dict, conv_cache, ssm_state, threads: int = 
         Bsz, E, N, K, _ptr(x), _ptr(z), _ptr(dtr), _ptr(Bm), _ptr(Cm), _ptr(A_log),
         _ptr(_f32(params["D"])), _ptr(_f32(params["dt_bias"])), _ptr(w),
         _ptr(_f32(params["conv_b"])), float(params["dt_min"]), float(params["dt_max"]),
-        _ptr(conv_cache), _ptr(ssm_state), _ptr(y), int(threads),
+        *_variant(params), _ptr(conv_cache), _ptr(ssm_state), _ptr(y), int(threads),
     )
     if rc != 0:
         raise ValueError("oracle_ssm_decode_step rejected its arguments")

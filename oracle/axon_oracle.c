@@ -29,13 +29,15 @@ int oracle_ssm_channel(int64_t L, int64_t N, int64_t K,
                        const float* x, const float* z, const float* dt_raw, int64_t act_stride,
                        const float* Bm, const float* Cm, int64_t bc_stride,
                        const float* A_log, double D, double dt_bias, const float* conv_w,
-                       double conv_b, double dt_min, double dt_max,
+                       double conv_b, double dt_min, double dt_max, int conv_act, int disc,
                        const double* win_in, const double* h_in,
                        double* y, int64_t y_stride, double* win_out, double* h_out,
                        double* u_out, double* dt_out, double* mag_out) {
   if (L < 0 || N < 1 || K < 1 || N > 4096 || K > 64) return -1;
   if (L > 0 && (!x || !z || !dt_raw || !Bm || !Cm || !y)) return -1;
   if (!A_log || !conv_w || !win_out || !h_out) return -1;
+  if (conv_act != ORACLE_CONV_NONE && conv_act != ORACLE_CONV_SILU) return -1;
+  if (disc != ORACLE_DISC_FIRST_ORDER && disc != ORACLE_DISC_ZOH) return -1;
 
   /* Diagonal state matrix: A_n = -exp(A_log_n).  [AXON "Diagonal state matrix"] */
   double* A = (double*)malloc(sizeof(double) * (size_t)N);
@@ -64,6 +66,9 @@ int oracle_ssm_channel(int64_t L, int64_t N, int64_t K,
     u += (double)conv_w[K - 1] * xt;
     for (int64_t k = 0; k + 1 < K - 1; ++k) win[k] = win[k + 1];
     if (K > 1) win[K - 2] = xt;
+    /* Mamba-block variant: SiLU on the convolution output before the scan.
+     * ["Selective State Space Models (Mamba)", pattern "Mamba block" (mamba-ssm's block)] */
+    if (conv_act == ORACLE_CONV_SILU) u = silu(u);
 
     /* Step size: dt = softplus(dt_raw + b_dt), clipped to [dt_min, dt_max].
      * [AXON "Selective mechanism"] */
@@ -78,7 +83,11 @@ int oracle_ssm_channel(int64_t L, int64_t N, int64_t K,
     double acc = 0.0, mag = 0.0;
     for (int64_t n = 0; n < N; ++n) {
       const double abar = exp(dt * A[n]);
-      const double bbar = dt * (double)Bm[t * bc_stride + n];
+      /* Exact zero-order hold for a diagonal A: Bbar = (dt A)^-1 (exp(dt A) - 1) dt B
+       * = expm1(dt A) / A * B.  [AXON "ZOH discretization"; glossary "How SSMs work"] */
+      const double bbar = disc == ORACLE_DISC_ZOH
+                              ? expm1(dt * A[n]) / A[n] * (double)Bm[t * bc_stride + n]
+                              : dt * (double)Bm[t * bc_stride + n];
       h[n] = abar * h[n] + bbar * u;
       acc += (double)Cm[t * bc_stride + n] * h[n];
       mag += fabs((double)Cm[t * bc_stride + n] * h[n]);
@@ -108,6 +117,7 @@ typedef struct {
   int64_t Bsz, L, E, N, K;
   const float *x, *z, *dt_raw, *Bm, *Cm, *A_log, *D, *dt_bias, *conv_w, *conv_b;
   double dt_min, dt_max;
+  int conv_act, disc;
   const double *cache_in, *state_in;
   double *y, *cache_out, *state_out, *mag;
   int64_t ch_begin, ch_end; /* channel index c = b * E + e */
@@ -135,7 +145,7 @@ static void* prefill_worker(void* arg) {
         has_tokens ? j->dt_raw + off : NULL, E, has_tokens ? j->Bm + b * L * N : NULL,
         has_tokens ? j->Cm + b * L * N : NULL, N, j->A_log + e * N, (double)j->D[e],
         (double)j->dt_bias[e], j->conv_w + e * K, (double)j->conv_b[e], j->dt_min, j->dt_max,
-        win_in, h_in, has_tokens ? j->y + off : NULL, E, win_out, h_out, NULL, NULL,
+        j->conv_act, j->disc, win_in, h_in, has_tokens ? j->y + off : NULL, E, win_out, h_out, NULL, NULL,
         (has_tokens && j->mag) ? j->mag + off : NULL);
     for (int64_t k = 0; k < K - 1; ++k) j->cache_out[(b * (K - 1) + k) * E + e] = win_out[k];
     for (int64_t n = 0; n < N; ++n) j->state_out[(b * E + e) * N + n] = h_out[n];
@@ -179,6 +189,7 @@ int oracle_ssm_prefill(int64_t Bsz, int64_t L, int64_t E, int64_t N, int64_t K,
                        const float* Bm, const float* Cm,
                        const float* A_log, const float* D, const float* dt_bias,
                        const float* conv_w, const float* conv_b, double dt_min, double dt_max,
+                       int conv_act, int disc,
                        const double* conv_cache_in, const double* ssm_state_in,
                        double* y, double* conv_cache_out, double* ssm_state_out, double* mag,
                        int threads) {
@@ -191,6 +202,7 @@ int oracle_ssm_prefill(int64_t Bsz, int64_t L, int64_t E, int64_t N, int64_t K,
   proto.x = x; proto.z = z; proto.dt_raw = dt_raw; proto.Bm = Bm; proto.Cm = Cm;
   proto.A_log = A_log; proto.D = D; proto.dt_bias = dt_bias; proto.conv_w = conv_w;
   proto.conv_b = conv_b; proto.dt_min = dt_min; proto.dt_max = dt_max;
+  proto.conv_act = conv_act; proto.disc = disc;
   proto.cache_in = conv_cache_in; proto.state_in = ssm_state_in;
   proto.y = y; proto.cache_out = conv_cache_out; proto.state_out = ssm_state_out;
   proto.mag = mag;
@@ -202,11 +214,13 @@ int oracle_ssm_decode_step(int64_t Bsz, int64_t E, int64_t N, int64_t K,
                            const float* Bm, const float* Cm,
                            const float* A_log, const float* D, const float* dt_bias,
                            const float* conv_w, const float* conv_b, double dt_min, double dt_max,
+                           int conv_act, int disc,
                            double* conv_cache, double* ssm_state, double* y, int threads) {
   /* A decode step is the prefill body for a single token with the caches carried in place.
    * [AXON "Autoregressive decoding"] Each channel reads its own cache entries before writing
    * them, so passing the same arrays as input and output is safe. */
   return oracle_ssm_prefill(Bsz, 1, E, N, K, x, z, dt_raw, Bm, Cm, A_log, D, dt_bias, conv_w,
-                            conv_b, dt_min, dt_max, conv_cache, ssm_state, y, conv_cache,
+                            conv_b, dt_min, dt_max, conv_act, disc, conv_cache, ssm_state, y,
+                            conv_cache,
                             ssm_state, NULL, threads);
 }

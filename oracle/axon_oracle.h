@@ -18,6 +18,16 @@
 extern "C" {
 #endif
 
+/* Variants (section 8(f) of the build's scope: next rows beyond the Axon-SSM layer):
+ *   conv_act: ORACLE_CONV_NONE (Axon-SSM: u = conv(x)) or ORACLE_CONV_SILU (Mamba block:
+ *             u = SiLU(conv(x)); the skip term D u uses the same u)
+ *   disc:     ORACLE_DISC_FIRST_ORDER (Axon-SSM: Bbar = dt B) or ORACLE_DISC_ZOH (exact
+ *             zero-order hold for a diagonal A: Bbar = (exp(dt A) - 1) / A * B) */
+#define ORACLE_CONV_NONE 0
+#define ORACLE_CONV_SILU 1
+#define ORACLE_DISC_FIRST_ORDER 0
+#define ORACLE_DISC_ZOH 1
+
 /* One channel (one (b, e) pair) over L tokens.
  *   x, z, dt_raw : token t at [t * act_stride]
  *   Bm, Cm       : B_t,n at [t * bc_stride + n]
@@ -36,7 +46,7 @@ int oracle_ssm_channel(int64_t L, int64_t N, int64_t K,
                        const float* x, const float* z, const float* dt_raw, int64_t act_stride,
                        const float* Bm, const float* Cm, int64_t bc_stride,
                        const float* A_log, double D, double dt_bias, const float* conv_w,
-                       double conv_b, double dt_min, double dt_max,
+                       double conv_b, double dt_min, double dt_max, int conv_act, int disc,
                        const double* win_in, const double* h_in,
                        double* y, int64_t y_stride, double* win_out, double* h_out,
                        double* u_out, double* dt_out, double* mag_out);
@@ -52,6 +62,7 @@ int oracle_ssm_prefill(int64_t Bsz, int64_t L, int64_t E, int64_t N, int64_t K,
                        const float* Bm, const float* Cm,
                        const float* A_log, const float* D, const float* dt_bias,
                        const float* conv_w, const float* conv_b, double dt_min, double dt_max,
+                       int conv_act, int disc,
                        const double* conv_cache_in, const double* ssm_state_in,
                        double* y, double* conv_cache_out, double* ssm_state_out, double* mag,
                        int threads);
@@ -63,6 +74,7 @@ int oracle_ssm_decode_step(int64_t Bsz, int64_t E, int64_t N, int64_t K,
                            const float* Bm, const float* Cm,
                            const float* A_log, const float* D, const float* dt_bias,
                            const float* conv_w, const float* conv_b, double dt_min, double dt_max,
+                           int conv_act, int disc,
                            double* conv_cache, double* ssm_state, double* y, int threads);
 
 #ifdef __cplusplus

@@ -353,7 +353,125 @@ def pin_empty_sequence(lib=None):
     np.testing.assert_array_equal(r0["ssm_state"], 0.0)
 
 
+# ---- variants: exact zero-order hold, SiLU after the convolution -----------------------------
+def pin_zoh_glossary_worked_example(lib=None):
+    """With the exact zero-order-hold discretisation, the [GLOSS] worked example is reproduced
+    literally: the page's own A, B, C, delta (seed-0 torch draws), Bbar = (Abar - 1) / A B, and
+    y_t / SiLU(z_t) equal to the page's convolution form within the page's tolerance, and to the
+    closed form on the float32-rounded inputs to rounding."""
+    import torch
+
+    gd = golden("lti_recurrence_vs_convolution.json")
+    L, n, delta = gd["L"], gd["N"], gd["delta"]
+    torch.manual_seed(gd["torch_manual_seed"])
+    x = torch.randn(L).double().numpy()
+    A = (-(torch.rand(n) + 0.5)).double().numpy()
+    Bv = torch.randn(n).double().numpy()
+    Cv = torch.randn(n).double().numpy()
+    Abar = np.exp(delta * A)
+    y_conv_page = np.convolve(x, _lti_kernel(Abar, (Abar - 1.0) / A * Bv, Cv, L))[:L]
+
+    z = np.full((1, L, 1), 8.0, np.float32)
+    inp = {
+        "x": x.astype(np.float32).reshape(1, L, 1), "z": z,
+        "dt_raw": np.zeros((1, L, 1), np.float32),
+        "B": np.tile(Bv.astype(np.float32), (1, L, 1)),
+        "C": np.tile(Cv.astype(np.float32), (1, L, 1)),
+        "A_log": np.log(-A).astype(np.float32).reshape(1, n),
+        "D": np.zeros(1, np.float32), "dt_bias": np.zeros(1, np.float32),
+        "conv_w": np.array([[0, 0, 0, 1]], np.float32), "conv_b": np.zeros(1, np.float32),
+        "dt_min": delta, "dt_max": delta, "discretization": "zoh",
+    }
+    got = oracle.prefill(inp, lib=lib)["y"][0, :, 0] / _silu(z[0, :, 0])
+    xf = inp["x"][0, :, 0].astype(np.float64)
+    Af = -np.exp(inp["A_log"][0].astype(np.float64))
+    Abf = np.exp(delta * Af)
+    Kf = _lti_kernel(Abf, np.expm1(delta * Af) / Af * inp["B"][0, 0].astype(np.float64),
+                     inp["C"][0, 0].astype(np.float64), L)
+    np.testing.assert_allclose(got, np.convolve(xf, Kf)[:L], rtol=1e-11, atol=1e-12)
+    assert np.allclose(got, y_conv_page, atol=gd["atol"]), "page's verdict not reproduced (ZOH)"
+
+
+def pin_zoh_lti_closed_form(lib=None, L=48, seed=40):
+    """Constant B, C, dt and identity convolution with exact ZOH: y / SiLU(z) is the convolution
+    with K_k = C . Abar^k Bbar, Bbar = expm1(dt A) / A B; over a range of steps (where the
+    first-order and exact forms differ by up to a factor (1 - e^-x) / x)."""
+    for delta in (0.0009765625, 0.0625, 0.5, 4.0):   # exact in binary
+        inp, _ = _case(L, seed=seed)
+        g = np.random.default_rng(seed + 7)
+        Bc = g.standard_normal(N).astype(np.float32)
+        Cc = g.standard_normal(N).astype(np.float32)
+        inp["B"][:] = Bc
+        inp["C"][:] = Cc
+        inp["conv_w"][:] = np.array([0, 0, 0, 1], np.float32)
+        inp["conv_b"][:] = 0
+        inp["dt_min"] = inp["dt_max"] = delta
+        inp["discretization"] = "zoh"
+        r = oracle.prefill(inp, lib=lib)
+        A = -np.exp(inp["A_log"][0].astype(np.float64))
+        Kk = _lti_kernel(np.exp(delta * A), np.expm1(delta * A) / A * Bc.astype(np.float64),
+                         Cc.astype(np.float64), L)
+        x = inp["x"][0, :, 0].astype(np.float64)
+        expect = np.convolve(x, Kk)[:L] + float(inp["D"][0]) * x
+        got = r["y"][0, :, 0] / _silu(inp["z"][0, :, 0])
+        np.testing.assert_allclose(got, expect, rtol=1e-11, atol=1e-12)
+
+
+def pin_conv_silu(lib=None, L=20, seed=41):
+    """SiLU after the convolution (Mamba block): u = SiLU(conv_b + w correlated with
+    [cache, x]) (numpy correlate, then z sigmoid(z)), seen through the oracle's u output; the
+    cache still holds the raw inputs. With an identity conv, constant B, C, dt and h_0 = 0 the
+    layer is the LTI convolution of SiLU(x)."""
+    inp, extra = _case(L, E=2, seed=seed, cache=True)
+    inp["conv_activation"] = "silu"
+    for e in range(2):
+        c = oracle.channel(inp, 0, e, lib=lib, **extra)
+        full = np.concatenate([extra["conv_cache_in"][0, :, e],
+                               inp["x"][0, :, e].astype(np.float64)])
+        v = np.correlate(full, inp["conv_w"][e].astype(np.float64), mode="valid")
+        v += float(inp["conv_b"][e])
+        np.testing.assert_allclose(c["u"], v / (1.0 + np.exp(-v)), rtol=1e-14, atol=1e-14)
+        np.testing.assert_array_equal(c["conv_cache"], full[-(K - 1):])
+    inp, _ = _case(L, seed=seed + 1)
+    g = np.random.default_rng(seed + 2)
+    Bc = g.standard_normal(N).astype(np.float32)
+    Cc = g.standard_normal(N).astype(np.float32)
+    inp["B"][:] = Bc
+    inp["C"][:] = Cc
+    inp["conv_w"][:] = np.array([0, 0, 0, 1], np.float32)
+    inp["conv_b"][:] = 0
+    delta = 0.125
+    inp["dt_min"] = inp["dt_max"] = delta
+    inp["conv_activation"] = "silu"
+    r = oracle.prefill(inp, lib=lib)
+    A = -np.exp(inp["A_log"][0].astype(np.float64))
+    Kk = _lti_kernel(np.exp(delta * A), delta * Bc.astype(np.float64), Cc.astype(np.float64), L)
+    xs = _silu(inp["x"][0, :, 0].astype(np.float64))
+    expect = np.convolve(xs, Kk)[:L] + float(inp["D"][0]) * xs
+    got = r["y"][0, :, 0] / _silu(inp["z"][0, :, 0])
+    np.testing.assert_allclose(got, expect, rtol=1e-11, atol=1e-12)
+
+
+def pin_variants_decode_equals_prefill(lib=None):
+    """The decode = prefill and continuation invariants hold for every variant."""
+    for act in ("none", "silu"):
+        for disc in ("first_order", "zoh"):
+            inp, extra = _case(11, E=3, Bsz=2, seed=42, h0=True, cache=True)
+            inp["conv_activation"], inp["discretization"] = act, disc
+            full = oracle.prefill(inp, lib=lib, **extra)
+            r1 = oracle.prefill(_tokens(inp, 0, 6), lib=lib, **extra)
+            cache, state = r1["conv_cache"].copy(), r1["ssm_state"].copy()
+            ys = []
+            for t in range(6, 11):
+                step = {k: inp[k][:, t] for k in ("x", "z", "dt_raw", "B", "C")}
+                ys.append(oracle.decode_step(step, inp, cache, state, lib=lib))
+            np.testing.assert_array_equal(np.stack(ys, axis=1), full["y"][:, 6:])
+            np.testing.assert_array_equal(state, full["ssm_state"])
+
+
 ALL_PINS = [
+    pin_zoh_glossary_worked_example, pin_zoh_lti_closed_form, pin_conv_silu,
+    pin_variants_decode_equals_prefill,
     pin_lti_closed_form, pin_glossary_worked_example, pin_zero_input_decay, pin_dt_clip_bounds,
     pin_softplus_values, pin_A_from_A_log, pin_conv_shift, pin_conv_correlation,
     pin_brute_force, pin_decode_equals_prefill, pin_prefill_continuation, pin_empty_sequence,

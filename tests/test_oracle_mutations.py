@@ -16,10 +16,18 @@ MUTATIONS = {
     "drop_D_skip": ("acc += D * u;", "acc += 0.0 * D * u;"),
     "positive_A": ("A[n] = -exp((double)A_log[n]);", "A[n] = exp((double)A_log[n]);"),
     "A_without_exp": ("A[n] = -exp((double)A_log[n]);", "A[n] = -(double)A_log[n];"),
-    "bbar_without_dt": ("const double bbar = dt * (double)Bm[t * bc_stride + n];",
-                        "const double bbar = (double)Bm[t * bc_stride + n];"),
-    "B_C_swapped": ("const double bbar = dt * (double)Bm[t * bc_stride + n];",
-                    "const double bbar = dt * (double)Cm[t * bc_stride + n];"),
+    "bbar_without_dt": (": dt * (double)Bm[t * bc_stride + n];",
+                        ": (double)Bm[t * bc_stride + n];"),
+    "B_C_swapped": (": dt * (double)Bm[t * bc_stride + n];",
+                    ": dt * (double)Cm[t * bc_stride + n];"),
+    "zoh_exp_not_expm1": ("? expm1(dt * A[n]) / A[n]", "? exp(dt * A[n]) / A[n]"),
+    "zoh_without_divide": ("? expm1(dt * A[n]) / A[n]", "? expm1(dt * A[n])"),
+    "zoh_is_first_order": ("? expm1(dt * A[n]) / A[n] * (double)Bm[t * bc_stride + n]",
+                           "? dt * (double)Bm[t * bc_stride + n]"),
+    "conv_silu_dropped": ("if (conv_act == ORACLE_CONV_SILU) u = silu(u);",
+                          "if (conv_act == ORACLE_CONV_SILU) u = u;"),
+    "conv_silu_on_current_input_only": ("if (conv_act == ORACLE_CONV_SILU) u = silu(u);",
+                                        "if (conv_act == ORACLE_CONV_SILU) u = u - xt + silu(xt);"),
     "readout_before_update": (
         "h[n] = abar * h[n] + bbar * u;\n      acc += (double)Cm[t * bc_stride + n] * h[n];",
         "acc += (double)Cm[t * bc_stride + n] * h[n];\n      h[n] = abar * h[n] + bbar * u;"),
