@@ -91,7 +91,20 @@ typedef struct {
   const float* conv_b;   /* (E)    */
   float dt_min;          /* lower clip of dt; the Axon-SSM page uses 1e-4 */
   float dt_max;          /* upper clip of dt; the Axon-SSM page uses 100  */
+  /* Variants; zero (the default of a zero-initialised struct) is the Axon-SSM layer.
+   *   conv_activation: AXON_CONV_NONE, or AXON_CONV_SILU: u = SiLU(conv(x)) before the scan
+   *     (the Mamba block of "Selective State Space Models (Mamba)", pattern "Mamba block"); the
+   *     skip term D u uses the same u, and conv_cache still holds the raw inputs.
+   *   discretization: AXON_DISC_FIRST_ORDER (Bbar = dt B, [AXON "ZOH discretization"]), or
+   *     AXON_DISC_ZOH: the exact zero-order hold for the diagonal A that the same section
+   *     states first, Bbar = expm1(dt A) / A * B.
+   * Other values: AXON_ERR_UNSUPPORTED. */
+  int32_t conv_activation;
+  int32_t discretization;
 } axon_ssm_params;
+
+enum { AXON_CONV_NONE = 0, AXON_CONV_SILU = 1 };
+enum { AXON_DISC_FIRST_ORDER = 0, AXON_DISC_ZOH = 1 };
 
 /* Library version as 10000*major + 100*minor + patch. */
 int axon_version(void);

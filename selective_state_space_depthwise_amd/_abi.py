@@ -41,7 +41,11 @@ class Shape(ctypes.Structure):
 class Params(ctypes.Structure):
     _fields_ = [("A_log", ctypes.c_void_p), ("D", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
                 ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p),
-                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float)]
+                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float),
+                ("conv_activation", ctypes.c_int32), ("discretization", ctypes.c_int32)]
+
+CONV_ACTIVATIONS = {"none": 0, "silu": 1}
+DISCRETIZATIONS = {"first_order": 0, "zoh": 1}
 
 
 _lock = threading.Lock()
@@ -90,8 +94,13 @@ def make_shape(batch, seqlen, d_inner, act_bf16, d_state=16, d_conv=4) -> Shape:
                  AXON_BF16 if act_bf16 else AXON_F32)
 
 
-def make_params(A_log, D, dt_bias, conv_w, conv_b, dt_min, dt_max) -> Params:
-    return Params(A_log, D, dt_bias, conv_w, conv_b, float(dt_min), float(dt_max))
+def make_params(A_log, D, dt_bias, conv_w, conv_b, dt_min, dt_max, conv_activation="none",
+                discretization="first_order") -> Params:
+    """Parameter block; variant names as in CONV_ACTIVATIONS / DISCRETIZATIONS, or raw ints
+    (passed through unchecked, so the library's own validation can be exercised)."""
+    act = conv_activation if isinstance(conv_activation, int) else CONV_ACTIVATIONS[conv_activation]
+    disc = discretization if isinstance(discretization, int) else DISCRETIZATIONS[discretization]
+    return Params(A_log, D, dt_bias, conv_w, conv_b, float(dt_min), float(dt_max), act, disc)
 
 
 def workspace_bytes(shape: Shape) -> int:

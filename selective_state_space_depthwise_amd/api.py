@@ -41,12 +41,14 @@ def _check(t: torch.Tensor, name: str, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _params(A_log, D, dt_bias, conv_w, conv_b, dt_min, dt_max, E, device):
+def _params(A_log, D, dt_bias, conv_w, conv_b, dt_min, dt_max, E, device,
+            conv_activation="none", discretization="first_order"):
     for t, n, shp in ((A_log, "A_log", (E, D_STATE)), (D, "D", (E,)), (dt_bias, "dt_bias", (E,)),
                       (conv_w, "conv_w", (E, D_CONV)), (conv_b, "conv_b", (E,))):
         _check(t, n, shp, torch.float32, device)
     return _abi.make_params(A_log.data_ptr(), D.data_ptr(), dt_bias.data_ptr(),
-                            conv_w.data_ptr(), conv_b.data_ptr(), dt_min, dt_max)
+                            conv_w.data_ptr(), conv_b.data_ptr(), dt_min, dt_max,
+                            conv_activation, discretization)
 
 
 def prefill_workspace_bytes(batch: int, seqlen: int, d_inner: int, bf16: bool = False) -> int:
@@ -56,14 +58,18 @@ def prefill_workspace_bytes(batch: int, seqlen: int, d_inner: int, bf16: bool = 
 
 def prefill(x, z, dt_raw, B, C, A_log, D, dt_bias, conv_w, conv_b, *, dt_min=1e-4, dt_max=100.0,
             conv_cache_in=None, ssm_state_in=None, y=None, conv_cache_out=None,
-            ssm_state_out=None, workspace=None, stream=None):
+            ssm_state_out=None, workspace=None, stream=None, conv_activation="none",
+            discretization="first_order"):
     """Run the layer over x, z, dt_raw (B, L, E) and B, C (B, L, N) on the GPU.
 
     Activations are float32 or bfloat16 (all the same dtype); parameters float32. Optional
     ``conv_cache_in`` (B, K-1, E) and ``ssm_state_in`` (B, E, N) are float32 (None = zeros).
     Outputs may be given (``y``, ``conv_cache_out``, ``ssm_state_out``; the caches may be the
     inputs themselves for an in-place update) or are allocated. Returns (y, conv_cache, ssm_state).
-    Asynchronous on ``stream`` (default: torch's current stream on x's device)."""
+    Asynchronous on ``stream`` (default: torch's current stream on x's device).
+    Variants: ``conv_activation`` "none" (Axon-SSM) or "silu" (SiLU on the convolution output,
+    the Mamba block); ``discretization`` "first_order" (Bbar = dt B) or "zoh" (exact zero-order
+    hold, Bbar = expm1(dt A) / A B)."""
     device = x.device
     if device.type != "cuda":
         raise ValueError("prefill runs on the GPU only; x is on " + str(device))
@@ -75,7 +81,8 @@ def prefill(x, z, dt_raw, B, C, A_log, D, dt_bias, conv_w, conv_b, *, dt_min=1e-
         _check(t, n, (Bsz, L, E), x.dtype, device)
     for t, n in ((B, "B"), (C, "C")):
         _check(t, n, (Bsz, L, D_STATE), x.dtype, device)
-    prm = _params(A_log, D, dt_bias, conv_w, conv_b, dt_min, dt_max, E, device)
+    prm = _params(A_log, D, dt_bias, conv_w, conv_b, dt_min, dt_max, E, device,
+                  conv_activation, discretization)
     cache_shape, state_shape = (Bsz, D_CONV - 1, E), (Bsz, E, D_STATE)
     if conv_cache_in is not None:
         _check(conv_cache_in, "conv_cache_in", cache_shape, torch.float32, device)
@@ -108,7 +115,8 @@ def prefill(x, z, dt_raw, B, C, A_log, D, dt_bias, conv_w, conv_b, *, dt_min=1e-
 
 
 def decode_step(x, z, dt_raw, B, C, A_log, D, dt_bias, conv_w, conv_b, conv_cache, ssm_state, *,
-                dt_min=1e-4, dt_max=100.0, y=None, stream=None):
+                dt_min=1e-4, dt_max=100.0, y=None, stream=None, conv_activation="none",
+                discretization="first_order"):
     """One token per batch row: x, z, dt_raw (B, E), B, C (B, N); conv_cache (B, K-1, E) and
     ssm_state (B, E, N) float32 are updated in place. Returns y (B, E)."""
     device = x.device
@@ -122,7 +130,8 @@ def decode_step(x, z, dt_raw, B, C, A_log, D, dt_bias, conv_w, conv_b, conv_cach
         _check(t, n, (Bsz, E), x.dtype, device)
     for t, n in ((B, "B"), (C, "C")):
         _check(t, n, (Bsz, D_STATE), x.dtype, device)
-    prm = _params(A_log, D, dt_bias, conv_w, conv_b, dt_min, dt_max, E, device)
+    prm = _params(A_log, D, dt_bias, conv_w, conv_b, dt_min, dt_max, E, device,
+                  conv_activation, discretization)
     _check(conv_cache, "conv_cache", (Bsz, D_CONV - 1, E), torch.float32, device)
     _check(ssm_state, "ssm_state", (Bsz, E, D_STATE), torch.float32, device)
     if y is None:

@@ -39,6 +39,7 @@ struct PrefillLaunch {
   const void *x, *z, *dt_raw, *B, *C;
   const float *A_log, *D, *dt_bias, *conv_w, *conv_b;
   float dt_min, dt_max;
+  int conv_silu, zoh;  // variants: SiLU after the conv; exact zero-order hold
   const float *conv_cache_in, *ssm_state_in;  // may be null (zeros)
   void* y;
   float *conv_cache_out, *ssm_state_out;
@@ -51,6 +52,7 @@ struct DecodeLaunch {
   const void *x, *z, *dt_raw, *B, *C;
   const float *A_log, *D, *dt_bias, *conv_w, *conv_b;
   float dt_min, dt_max;
+  int conv_silu, zoh;
   float *conv_cache, *ssm_state;
   void* y;
 };

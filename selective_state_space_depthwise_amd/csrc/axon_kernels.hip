@@ -48,6 +48,7 @@ struct DecodeArgs {
   const void *x, *z, *dt_raw, *Bm, *Cm;
   const float *A_log, *D, *dt_bias, *conv_w, *conv_b;
   float dt_min, dt_max;
+  int conv_silu, zoh;
   float *cache, *state;
   void* y;
 };
@@ -72,10 +73,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const float x2 = a.cache[(b * kHalo + 2) * a.E + e];
   const int64_t i = b * a.E + e;
   const float xv = load_act(x, i);
-  const float u = fmaf(a.conv_w[e * kConv + 3], xv,
-                       fmaf(a.conv_w[e * kConv + 2], x2,
-                            fmaf(a.conv_w[e * kConv + 1], x1,
-                                 fmaf(a.conv_w[e * kConv + 0], x0, a.conv_b[e]))));
+  float u = fmaf(a.conv_w[e * kConv + 3], xv,
+                 fmaf(a.conv_w[e * kConv + 2], x2,
+                      fmaf(a.conv_w[e * kConv + 1], x1,
+                           fmaf(a.conv_w[e * kConv + 0], x0, a.conv_b[e]))));
+  if (a.conv_silu) u = silu(u);  // Mamba-block variant: SiLU on the convolution output
   const float dt = step_size(load_act(dtr, i) + a.dt_bias[e], a.dt_min, a.dt_max);
   const float dtu = dt * u;
 
@@ -85,9 +87,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   float p = 0.0f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float rate = decay_rate_log2(a.A_log[e * kState + 4 * q + k]);
-    const float abar = __builtin_amdgcn_exp2f(dt * rate);
-    h[k] = fmaf(abar, h[k], dtu * load_act(Bp, k));
+    const float a_log = a.A_log[e * kState + 4 * q + k];
+    const float abar = __builtin_amdgcn_exp2f(dt * decay_rate_log2(a_log));
+    if (a.zoh) {
+      // Exact zero-order hold: Bbar = expm1(dt A) / A * B, A = -exp(A_log).
+      const float A = -expf(a_log);
+      h[k] = fmaf(abar, h[k], (expm1f(dt * A) / A) * u * load_act(Bp, k));
+    } else {
+      h[k] = fmaf(abar, h[k], dtu * load_act(Bp, k));
+    }
     p = fmaf(load_act(Cp, k), h[k], p);
   }
   p += __shfl_xor(p, 1);
@@ -122,6 +130,8 @@ int launch_decode_t(const DecodeLaunch& p, hipStream_t s) {
   a.conv_b = p.conv_b;
   a.dt_min = p.dt_min;
   a.dt_max = p.dt_max;
+  a.conv_silu = p.conv_silu;
+  a.zoh = p.zoh;
   a.cache = p.conv_cache;
   a.state = p.ssm_state;
   a.y = p.y;

@@ -223,6 +223,108 @@ __device__ __forceinline__ void scan_tile_from(const float4 (&dd)[kTile / 2],
   }
 }
 
+// ---- exact zero-order hold (variant) ---------------------------------------------------------
+// The input coefficient of a state becomes expm1(x) / A with x = dt A <= 0 instead of dt. With
+// y = x / ln 2 (the exp2 argument the decay already needs):
+//   |x| <  0.25: dt * phi, phi = expm1(x) / x = 1 + y (k1 + y (k2 + y (k3 + y k4))),
+//                k_j = ln2^j / (j + 1)! (the series cut after x^4: relative error < 1.4e-6);
+//   |x| >= 0.25: (a - 1) / A with a = exp(x), the decay itself (a - 1 no longer cancels).
+struct ZohConst {
+  float k1 = 0.34657359027997264f;    // ln 2 / 2
+  float k2 = 0.08007550231970023f;    // ln^2 2 / 6
+  float k3 = 0.013876027166205392f;   // ln^3 2 / 24
+  float k4 = 0.0019236258215256953f;  // ln^4 2 / 120
+  float thr = -0.36067376022224085f;  // y at x = -0.25
+};
+
+// One state of one token, exact zero-order hold, in this order:
+//   A  yn = dtn * rate, D  an = exp2(yn)        (next token's argument and decay, if any)
+//   P  p = dtc * phi(yc)                        (small-|x| coefficient of this token)
+//   Q  q = (ac - 1) / A, q = yc > thr ? p : q   (large-|x| coefficient, then the choice)
+//   B  b = bcast(RB, K) * uc                    (B of this token times its u)
+//   C  pp = bcast(RCp, KP) * h                  (readout product of the previous token)
+//   E  b = b * q + ac * h                       (the new state)
+// At least eight VALU instructions precede the first DPP instruction of the block.
+#define AXON_ZA "v_mul_f32 %[yn], %[dtn], %[r]\n\tv_exp_f32 %[an], %[yn]\n\t"
+#define AXON_ZP                                                                              \
+  "v_fma_f32 %[p], %[yc], %[k4], %[k3]\n\tv_fma_f32 %[p], %[yc], %[p], %[k2]\n\t"            \
+  "v_fma_f32 %[p], %[yc], %[p], %[k1]\n\tv_fma_f32 %[p], %[yc], %[p], 1.0\n\t"               \
+  "v_mul_f32 %[p], %[p], %[dtc]\n\t"                                                         \
+  "v_fma_f32 %[q], %[ac], %[ia], -%[ia]\n\tv_cmp_lt_f32 vcc, %[thr], %[yc]\n\t"              \
+  "v_cndmask_b32 %[q], %[q], %[p], vcc\n\t"
+#define AXON_ZB AXON_BC(b, RB, uc, k)
+#define AXON_ZC AXON_BC(pp, RCp, h, kp)
+#define AXON_ZE "v_mul_f32 %[b], %[b], %[q]\n\tv_fmac_f32 %[b], %[ac], %[h]\n\t"
+#define AXON_ZOUT [b] "=&v"(b), [an] "=&v"(an), [yn] "=&v"(yn), [pp] "=&v"(pp), [p] "=&v"(p), \
+                  [q] "=&v"(q)
+#define AXON_ZIN                                                                             \
+  [dtn] "v"(dtn), [dtc] "v"(dtc), [uc] "v"(uc), [RB] "v"(RB), [RCp] "v"(RCp), [k1] "v"(zc.k1), \
+      [k2] "v"(zc.k2), [k3] "v"(zc.k3), [k4] "v"(zc.k4), [thr] "v"(zc.thr), [r] "v"(r),        \
+      [ac] "v"(ac), [yc] "v"(yc), [ia] "v"(ia), [h] "v"(h), [k] "i"(K), [kp] "i"(KP)
+
+template <int K, int KP, bool kPrev, bool kNext>
+__device__ __forceinline__ void step_zoh(float dtn, float dtc, float uc, float r, float ac,
+                                         float yc, float ia, float RB, float RCp,
+                                         const ZohConst& zc, float& h, float& an, float& yn,
+                                         float& pp) {
+  float b, p, q;
+  if constexpr (kNext && kPrev)
+    asm(AXON_ZA AXON_ZP AXON_ZB AXON_ZC AXON_ZE : AXON_ZOUT : AXON_ZIN : "vcc");
+  else if constexpr (kNext)
+    asm(AXON_ZA AXON_ZP AXON_ZB AXON_ZE : AXON_ZOUT : AXON_ZIN : "vcc");
+  else if constexpr (kPrev)
+    asm(AXON_ZP AXON_ZB AXON_ZC AXON_ZE : AXON_ZOUT : AXON_ZIN : "vcc");
+  else
+    asm(AXON_ZP AXON_ZB AXON_ZE : AXON_ZOUT : AXON_ZIN : "vcc");
+  h = b;
+}
+
+// The tokens of a tile with the exact zero-order hold: as scan_tile_from, with dd holding
+// (dt, u) pairs and the arguments yc carried from block to block beside the decays ac.
+template <int SPL, bool kCarry, int TAU, int kTile>
+__device__ __forceinline__ void scan_tile_zoh_from(
+    const float4 (&dd)[kTile / 2], const float (&rate)[SPL], const float (&ia)[SPL],
+    const ZohConst& zc, const float (&RB)[kTile * SPL / 16], const float (&RC)[kTile * SPL / 16],
+    float (&h)[SPL], float (&ac)[SPL], float (&yc)[SPL], float (&P)[kTile], float& S) {
+  constexpr int TPR = 16 / SPL;
+  constexpr int J = TAU / TPR;
+  constexpr int K = (TAU % TPR) * SPL;
+  constexpr int JP = (TAU > 0 ? TAU - 1 : 0) / TPR;
+  constexpr int KP = ((TAU > 0 ? TAU - 1 : 0) % TPR) * SPL;
+  constexpr int TN = TAU + 1 < kTile ? TAU + 1 : TAU;
+  const float dtc = (TAU & 1) ? dd[TAU / 2].z : dd[TAU / 2].x;
+  const float uc = (TAU & 1) ? dd[TAU / 2].w : dd[TAU / 2].y;
+  const float dtn = (TN & 1) ? dd[TN / 2].z : dd[TN / 2].x;
+  if constexpr (TAU == 0) {
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+      asm("v_mul_f32 %[y], %[dt], %[r]\n\tv_exp_f32 %[a], %[y]"
+          : [y] "=&v"(yc[i]), [a] "=&v"(ac[i]) : [dt] "v"(dtc), [r] "v"(rate[i]));
+    if constexpr (kCarry) S += dtc;
+  }
+  if constexpr (kCarry && TAU + 1 < kTile) S += dtn;
+  constexpr bool kPrev = !kCarry && TAU >= 1;
+  constexpr bool kNext = TAU + 1 < kTile;
+  float an[SPL], yn[SPL], pp[SPL];
+  step_zoh<K, KP, kPrev, kNext>(dtn, dtc, uc, rate[0], ac[0], yc[0], ia[0], RB[J], RC[JP], zc,
+                                h[0], an[0], yn[0], pp[0]);
+  if constexpr (SPL == 2)
+    step_zoh<K + 1, KP + 1, kPrev, kNext>(dtn, dtc, uc, rate[1], ac[1], yc[1], ia[1], RB[J],
+                                          RC[JP], zc, h[1], an[1], yn[1], pp[1]);
+  if constexpr (kPrev) P[TAU - 1] = lane_sum<SPL>(pp);
+  if constexpr (kNext) {
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      ac[i] = an[i];
+      yc[i] = yn[i];
+    }
+    scan_tile_zoh_from<SPL, kCarry, TAU + 1, kTile>(dd, rate, ia, zc, RB, RC, h, ac, yc, P, S);
+  } else if constexpr (!kCarry) {
+    flush<SPL, ((kTile - 1) % TPR) * SPL>(RC[kTile * SPL / 16 - 1], h, pp);
+    P[kTile - 1] = lane_sum<SPL>(pp);
+  }
+}
+
 // Sum of four tokens' products over the 4 lane rows: on return, row q holds token q's sum.
 __device__ __forceinline__ float rows_reduce4(float p0, float p1, float p2, float p3) {
   const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2),
@@ -247,7 +349,8 @@ struct TileIn {
   float RB[NR], RC[NR];
 };
 
-template <typename Act, int W, bool kCarry>
+// kSilu: SiLU on the convolution output (Mamba-block variant); kZoh: exact zero-order hold.
+template <typename Act, int W, bool kCarry, bool kSilu, bool kZoh>
 __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
   constexpr int SPL = 4 / W;  // states per lane
   constexpr int kTile = tile_tokens<W>();
@@ -312,11 +415,13 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
   for (int j = 0; j < NR; ++j)
     bcoff[j] = static_cast<uint32_t>((j * TPR + c / SPL) * kState + g * SPL + (c % SPL)) * kElt;
 
-  float rate[SPL], h[SPL];
+  float rate[SPL], h[SPL], ia[SPL];  // ia: 1 / A_n (exact zero-order hold only)
+  const ZohConst zc;
 #pragma unroll
   for (int i = 0; i < SPL; ++i) {
     const int n = g * SPL + i;
     rate[i] = valid ? decay_rate_log2(a.A_log[e * kState + n]) : 0.0f;
+    ia[i] = valid ? -expf(-a.A_log[e * kState + n]) : 0.0f;
     h[i] = (a.h_src && valid) ? a.h_src[chunk * a.h_chunk_stride + (b * E + e) * kState + n]
                               : 0.0f;
   }
@@ -410,12 +515,13 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
     float pair[2 * TPL];
 #pragma unroll
     for (int r = 0; r < TPL; ++r) {
-      const float uu = fmaf(w3, in.xw[r + 3],
-                            fmaf(w2, in.xw[r + 2], fmaf(w1, in.xw[r + 1], fmaf(w0, in.xw[r], cb))));
+      float uu = fmaf(w3, in.xw[r + 3],
+                      fmaf(w2, in.xw[r + 2], fmaf(w1, in.xw[r + 1], fmaf(w0, in.xw[r], cb))));
+      if constexpr (kSilu) uu = silu(uu);
       const float keep = (valid && tau0 + r < rem) ? 1.0f : 0.0f;
       const float dt = step_size(in.dr[r] + dtb, a.dt_min, a.dt_max) * keep;
       pair[2 * r] = dt;
-      pair[2 * r + 1] = dt * uu;
+      pair[2 * r + 1] = kZoh ? uu : dt * uu;  // the exact hold scales u per state in the scan
       u[r] = uu;
     }
 #pragma unroll
@@ -452,7 +558,12 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
     for (int i = 0; i < kTile / 2; ++i)
       dd[i] = *reinterpret_cast<const float4*>(&s_dt[buf][slot][4 * i]);
     float P[kTile], ac[SPL];
-    scan_tile_from<SPL, kCarry, 0, kTile>(dd, rate, cur.RB, cur.RC, h, ac, P, S);
+    if constexpr (kZoh) {
+      float yc[SPL];
+      scan_tile_zoh_from<SPL, kCarry, 0, kTile>(dd, rate, ia, zc, cur.RB, cur.RC, h, ac, yc, P, S);
+    } else {
+      scan_tile_from<SPL, kCarry, 0, kTile>(dd, rate, cur.RB, cur.RC, h, ac, P, S);
+    }
 
     float u_next[TPL];
     if (k + 1 < ntiles) prologue(ts + kTile, nxt, buf ^ 1, u_next);
@@ -525,7 +636,7 @@ void launch_carry_combine(int64_t B, int64_t E, int64_t M, const float* A_log,
                           const float* state_in, const float* carry_h, const float* carry_s,
                           float* carry_in, hipStream_t s);
 
-template <typename Act, int W>
+template <typename Act, int W, bool kSilu, bool kZoh>
 int launch_row_scan_t(const PrefillLaunch& p, const PrefillPlan& plan, hipStream_t s) {
   RowArgs a{};
   a.B = p.batch;
@@ -555,7 +666,7 @@ int launch_row_scan_t(const PrefillLaunch& p, const PrefillPlan& plan, hipStream
     a.win_src = p.conv_cache_in;
     a.h_src = p.ssm_state_in;
     a.h_chunk_stride = 0;
-    hipLaunchKernelGGL((row_scan_kernel<Act, W, false>), dim3(gx, gy, 1), block, 0, s, a);
+    hipLaunchKernelGGL((row_scan_kernel<Act, W, false, kSilu, kZoh>), dim3(gx, gy, 1), block, 0, s, a);
     return static_cast<int>(hipGetLastError());
   }
   char* ws = static_cast<char*>(p.workspace);
@@ -566,26 +677,39 @@ int launch_row_scan_t(const PrefillLaunch& p, const PrefillPlan& plan, hipStream
   a.win_src = p.conv_cache_in;
   a.h_src = nullptr;
   a.h_chunk_stride = 0;
-  hipLaunchKernelGGL((row_scan_kernel<Act, W, true>),
+  hipLaunchKernelGGL((row_scan_kernel<Act, W, true, kSilu, kZoh>),
                      dim3(gx, gy, static_cast<unsigned>(plan.chunks - 1)), block, 0, s, a);
   launch_carry_combine(p.batch, p.d_inner, plan.chunks, p.A_log, p.ssm_state_in, a.carry_h,
                        a.carry_s, carry_in, s);
   a.win_src = a.halo;
   a.h_src = carry_in;
   a.h_chunk_stride = p.batch * p.d_inner * kState;
-  hipLaunchKernelGGL((row_scan_kernel<Act, W, false>),
+  hipLaunchKernelGGL((row_scan_kernel<Act, W, false, kSilu, kZoh>),
                      dim3(gx, gy, static_cast<unsigned>(plan.chunks)), block, 0, s, a);
   return static_cast<int>(hipGetLastError());
 }
 
+template <typename Act, bool kSilu, bool kZoh>
+int launch_row_scan_w(const PrefillLaunch& p, const PrefillPlan& plan, hipStream_t s) {
+  return plan.row_waves == 4 ? launch_row_scan_t<Act, 4, kSilu, kZoh>(p, plan, s)
+                             : launch_row_scan_t<Act, 2, kSilu, kZoh>(p, plan, s);
+}
+
+template <typename Act>
+int launch_row_scan_v(const PrefillLaunch& p, const PrefillPlan& plan, hipStream_t s) {
+  if (p.conv_silu)
+    return p.zoh ? launch_row_scan_w<Act, true, true>(p, plan, s)
+                 : launch_row_scan_w<Act, true, false>(p, plan, s);
+  return p.zoh ? launch_row_scan_w<Act, false, true>(p, plan, s)
+               : launch_row_scan_w<Act, false, false>(p, plan, s);
+}
+
 int launch_row_scan(const PrefillLaunch& p, const PrefillPlan& plan, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // The planner picks W = 4 (one state per lane) or W = 2 (two states per lane).
-  if (plan.row_waves == 4)
-    return p.act_bf16 ? launch_row_scan_t<bf16_bits, 4>(p, plan, s)
-                      : launch_row_scan_t<float, 4>(p, plan, s);
-  return p.act_bf16 ? launch_row_scan_t<bf16_bits, 2>(p, plan, s)
-                    : launch_row_scan_t<float, 2>(p, plan, s);
+  // The planner picks W = 4 (one state per lane) or W = 2 (two states per lane); the variants
+  // are compile-time so that the Axon-SSM kernel carries none of their code.
+  return p.act_bf16 ? launch_row_scan_v<bf16_bits>(p, plan, s)
+                    : launch_row_scan_v<float>(p, plan, s);
 }
 
 }  // namespace axon

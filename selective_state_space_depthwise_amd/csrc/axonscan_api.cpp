@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0: variant fields in axon_ssm_params
 constexpr int64_t kMaxBatch = 65535;      // launch grid y dimension
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 // The prefill kernels address a tile of (32 + 3) tokens x d_inner channels with byte offsets
@@ -80,6 +80,9 @@ axon_status check_params(const axon_ssm_params* p) {
   if (!std::isfinite(p->dt_min) || !std::isfinite(p->dt_max) || p->dt_min < 0.0f ||
       p->dt_min > p->dt_max)
     return AXON_ERR_INVALID_ARGUMENT;
+  if ((p->conv_activation != AXON_CONV_NONE && p->conv_activation != AXON_CONV_SILU) ||
+      (p->discretization != AXON_DISC_FIRST_ORDER && p->discretization != AXON_DISC_ZOH))
+    return AXON_ERR_UNSUPPORTED;
   return AXON_OK;
 }
 
@@ -145,7 +148,7 @@ const char* axon_status_string(axon_status status) {
   switch (status) {
     case AXON_OK: return "ok";
     case AXON_ERR_INVALID_ARGUMENT: return "invalid argument";
-    case AXON_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case AXON_ERR_UNSUPPORTED: return "unsupported shape, dtype or variant";
     case AXON_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case AXON_ERR_HIP: return "HIP launch or runtime error";
   }
@@ -240,6 +243,8 @@ axon_status axon_ssm_prefill(const axon_ssm_shape* shape, const axon_ssm_params*
   a.conv_b = params->conv_b;
   a.dt_min = params->dt_min;
   a.dt_max = params->dt_max;
+  a.conv_silu = params->conv_activation == AXON_CONV_SILU;
+  a.zoh = params->discretization == AXON_DISC_ZOH;
   a.conv_cache_in = conv_cache_in;
   a.ssm_state_in = ssm_state_in;
   a.y = y;
@@ -294,6 +299,8 @@ axon_status axon_ssm_decode_step(const axon_ssm_shape* shape, const axon_ssm_par
   a.conv_b = params->conv_b;
   a.dt_min = params->dt_min;
   a.dt_max = params->dt_max;
+  a.conv_silu = params->conv_activation == AXON_CONV_SILU;
+  a.zoh = params->discretization == AXON_DISC_ZOH;
   a.conv_cache = conv_cache;
   a.ssm_state = ssm_state;
   a.y = y;

@@ -17,6 +17,9 @@ import sys
 import numpy as np
 import torch
 
+import oracle
+import workloads
+
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 # The state is fp32 in both cases; for bf16 runs its error is set by the same fp32 arithmetic.
 STATE_TOL = {"f32": 1e-4, "bf16": 1e-4}
@@ -117,4 +120,49 @@ def single_channel_inputs(params: dict, e: int, seq: dict) -> dict:
         "dt_bias": params["dt_bias"][e:e + 1], "conv_w": params["conv_w"][e:e + 1],
         "conv_b": params["conv_b"][e:e + 1], "dt_min": params["dt_min"],
         "dt_max": params["dt_max"],
+        **{k: params[k] for k in ("conv_activation", "discretization") if k in params},
     }
+
+
+def make_case(B, L, E, act="f32", dt_mode="axon", seed=0, caches=False):
+    """Seeded inputs with the workloads' recipe at a given size, plus optional caches."""
+    w = workloads.Workload(0, "case", "prefill", B, L, E, act, dt_mode=dt_mode)
+    inp = workloads.prefill_inputs(w, seed_offset=seed)
+    extra = {}
+    if caches:
+        g = np.random.default_rng(1000 + seed)
+        cache = g.standard_normal((B, 3, E)).astype(np.float32)
+        if act == "bf16":
+            cache = workloads.bf16_round(cache)
+        extra["conv_cache_in"] = cache
+        extra["ssm_state_in"] = g.standard_normal((B, E, 16)).astype(np.float32)
+    return inp, extra
+
+
+def run_and_compare(inp, extra, what, inplace=False, conditioned=False):
+    """Run the HIP prefill through the binding and compare y, state (tolerance) and cache
+    (bit-exact) with the oracle. Variant keys of ``inp`` (conv_activation, discretization) are
+    passed to both."""
+    act = inp["act"]
+    variant = {k: inp[k] for k in ("conv_activation", "discretization") if k in inp}
+    say(f"[parity] {what}: B={inp['x'].shape[0]} L={inp['x'].shape[1]} E={inp['x'].shape[2]} "
+        f"act={act} caches={bool(extra)} inplace={inplace} {variant}")
+    d = to_device(inp)
+    kw = dict(variant)
+    cin = sin = None
+    if extra:
+        cin = torch.from_numpy(extra["conv_cache_in"]).cuda()
+        sin = torch.from_numpy(extra["ssm_state_in"]).cuda()
+        kw.update(conv_cache_in=cin, ssm_state_in=sin)
+        if inplace:
+            kw.update(conv_cache_out=cin, ssm_state_out=sin)
+    y, cache, state = gpu_prefill(d, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(inp, conv_cache_in=extra.get("conv_cache_in"),
+                         ssm_state_in=extra.get("ssm_state_in"), threads=8,
+                         magnitude=conditioned)
+    assert_close(host(y), ref["y"], TOL[act], f"{what}: y",
+                 mag=ref["mag"] if conditioned else None)
+    assert_close(host(state), ref["ssm_state"], STATE_TOL[act], f"{what}: ssm_state")
+    np.testing.assert_array_equal(host(cache), ref["conv_cache"], err_msg=f"{what}: conv_cache")
+    return d, y, cache, state, ref

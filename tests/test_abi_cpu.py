@@ -53,7 +53,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert A.version() == 100
+    assert A.version() == 200
     for st in range(5):
         assert A.status_string(st)
     assert A.status_string(99) == "unknown status"
@@ -94,6 +94,14 @@ def test_workspace_is_a_pure_function_of_shape():
 ])
 def test_prefill_rejects_bad_shapes(kw, status):
     assert _prefill(shape=_shape(**kw)) == status
+
+
+@pytest.mark.parametrize("act,disc", [(2, 0), (-1, 0), (0, 2), (0, -1), (7, 9)])
+def test_unknown_variants_are_unsupported(act, disc):
+    prm = A.make_params(*([P + (1 << 30) + i * (1 << 20) for i in range(5)]), 1e-4, 100.0,
+                        conv_activation=act, discretization=disc)
+    assert _prefill(params=prm) == A.AXON_ERR_UNSUPPORTED
+    assert _decode(params=prm) == A.AXON_ERR_UNSUPPORTED
 
 
 def test_prefill_rejects_unknown_dtype():

@@ -12,8 +12,8 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import (STATE_TOL, TOL, assert_close, gpu_decode, gpu_prefill, host, say,
-                      sample_channels, single_channel_inputs, to_device)
+from gpu_util import (STATE_TOL, TOL, assert_close, gpu_decode, gpu_prefill, host, make_case,
+                      run_and_compare, say, sample_channels, single_channel_inputs, to_device)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -28,45 +28,6 @@ def _gpu():
     axon.load()  # fails loudly when the library is missing
     yield
     torch.cuda.synchronize()
-
-
-def _case(B, L, E, act="f32", dt_mode="axon", seed=0, caches=False):
-    w = workloads.Workload(0, "case", "prefill", B, L, E, act, dt_mode=dt_mode)
-    inp = workloads.prefill_inputs(w, seed_offset=seed)
-    extra = {}
-    if caches:
-        g = np.random.default_rng(1000 + seed)
-        cache = g.standard_normal((B, 3, E)).astype(np.float32)
-        if act == "bf16":
-            cache = workloads.bf16_round(cache)
-        extra["conv_cache_in"] = cache
-        extra["ssm_state_in"] = g.standard_normal((B, E, 16)).astype(np.float32)
-    return inp, extra
-
-
-def _run_and_compare(inp, extra, what, inplace=False, conditioned=False):
-    act = inp["act"]
-    say(f"[parity] {what}: B={inp['x'].shape[0]} L={inp['x'].shape[1]} E={inp['x'].shape[2]} "
-        f"act={act} caches={bool(extra)} inplace={inplace}")
-    d = to_device(inp)
-    kw = {}
-    cin = sin = None
-    if extra:
-        cin = torch.from_numpy(extra["conv_cache_in"]).cuda()
-        sin = torch.from_numpy(extra["ssm_state_in"]).cuda()
-        kw = {"conv_cache_in": cin, "ssm_state_in": sin}
-        if inplace:
-            kw.update(conv_cache_out=cin, ssm_state_out=sin)
-    y, cache, state = gpu_prefill(d, **kw)
-    torch.cuda.synchronize()
-    ref = oracle.prefill(inp, conv_cache_in=extra.get("conv_cache_in"),
-                         ssm_state_in=extra.get("ssm_state_in"), threads=8,
-                         magnitude=conditioned)
-    assert_close(host(y), ref["y"], TOL[act], f"{what}: y",
-                 mag=ref["mag"] if conditioned else None)
-    assert_close(host(state), ref["ssm_state"], STATE_TOL[act], f"{what}: ssm_state")
-    np.testing.assert_array_equal(host(cache), ref["conv_cache"], err_msg=f"{what}: conv_cache")
-    return d, y, cache, state, ref
 
 
 SMALL = [
@@ -90,20 +51,20 @@ SMALL = [
 
 @pytest.mark.parametrize("B,L,E,act,dt_mode,caches", SMALL)
 def test_small_cases_match_oracle(B, L, E, act, dt_mode, caches):
-    inp, extra = _case(B, L, E, act, dt_mode, seed=B * 7 + L, caches=caches)
+    inp, extra = make_case(B, L, E, act, dt_mode, seed=B * 7 + L, caches=caches)
     # fp32 with dt clip hits is a stress case outside the workloads (see gpu_util)
-    _run_and_compare(inp, extra, f"small {B}x{L}x{E} {act} {dt_mode}",
+    run_and_compare(inp, extra, f"small {B}x{L}x{E} {act} {dt_mode}",
                      conditioned=(act == "f32" and dt_mode == "wide"))
 
 
 @pytest.mark.parametrize("L", [3, 900])
 def test_in_place_caches(L):
-    inp, extra = _case(2, L, 96, "f32", seed=5, caches=True)
-    _run_and_compare(inp, extra, f"in-place L={L}", inplace=True)
+    inp, extra = make_case(2, L, 96, "f32", seed=5, caches=True)
+    run_and_compare(inp, extra, f"in-place L={L}", inplace=True)
 
 
 def test_empty_sequence_copies_caches():
-    inp, extra = _case(2, 0, 80, "f32", seed=9, caches=True)
+    inp, extra = make_case(2, 0, 80, "f32", seed=9, caches=True)
     say("[parity] empty sequence")
     d = to_device(inp)
     cin = torch.from_numpy(extra["conv_cache_in"]).cuda()
@@ -120,15 +81,15 @@ def test_empty_sequence_copies_caches():
 
 @pytest.mark.parametrize("raw", [-1000.0, 1000.0, -50.0, 50.0])
 def test_dt_clip_extremes(raw):
-    inp, extra = _case(1, 300, 64, "f32", seed=11, caches=True)
+    inp, extra = make_case(1, 300, 64, "f32", seed=11, caches=True)
     inp["dt_raw"][:, ::3, :] = np.float32(raw)
-    _run_and_compare(inp, extra, f"dt_raw={raw}", conditioned=raw > 0)
+    run_and_compare(inp, extra, f"dt_raw={raw}", conditioned=raw > 0)
 
 
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 def test_prefill_continuation(act):
     """Prefill L1 tokens, then L2 more from the returned caches == the oracle over L1 + L2."""
-    inp, extra = _case(2, 1200, 72, act, seed=13, caches=True)
+    inp, extra = make_case(2, 1200, 72, act, seed=13, caches=True)
     L1 = 700
     say(f"[parity] continuation {act}")
     d = to_device(inp)
@@ -150,8 +111,8 @@ def test_workspace_reuse():
     """The same workspace tensor serves consecutive calls (contents need no initialisation)."""
     import selective_state_space_depthwise_amd as axon
 
-    inp_a, _ = _case(1, 1000, 64, "f32", seed=21)
-    inp_b, _ = _case(1, 1000, 64, "f32", seed=22)
+    inp_a, _ = make_case(1, 1000, 64, "f32", seed=21)
+    inp_b, _ = make_case(1, 1000, 64, "f32", seed=22)
     ws = torch.full((axon.prefill_workspace_bytes(1, 1000, 64),), 0xAB, dtype=torch.uint8,
                     device="cuda")
     for inp in (inp_a, inp_b, inp_a):
@@ -165,7 +126,7 @@ def test_decode_steps_match_oracle(act):
     """A prefill, then single-token decode steps with in-place caches; every step's y and the
     final caches against the oracle's decode steps."""
     B, E, L0, steps = 3, 100, 20, 12
-    inp, extra = _case(B, L0, E, act, seed=31, caches=True)
+    inp, extra = make_case(B, L0, E, act, seed=31, caches=True)
     say(f"[parity] decode {act}")
     d = to_device(inp)
     _, cache, state = gpu_prefill(d, conv_cache_in=torch.from_numpy(extra["conv_cache_in"]).cuda(),
@@ -189,7 +150,7 @@ def test_decode_steps_match_oracle(act):
 def test_decode_equals_prefill_on_gpu():
     """GPU decode, token by token, agrees with one GPU prefill over the same tokens."""
     B, E, L = 2, 130, 9
-    inp, extra = _case(B, L, E, "f32", seed=41, caches=True)
+    inp, extra = make_case(B, L, E, "f32", seed=41, caches=True)
     d = to_device(inp)
     cin = torch.from_numpy(extra["conv_cache_in"]).cuda()
     sin = torch.from_numpy(extra["ssm_state_in"]).cuda()
