@@ -100,6 +100,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device copy of known size (counter calibration)")
+    ap.add_argument("--conv-activation", default="none", choices=["none", "silu"],
+                    help="variant: SiLU on the convolution output (Mamba block)")
+    ap.add_argument("--discretization", default="first_order", choices=["first_order", "zoh"],
+                    help="variant: exact zero-order hold")
+    ap.add_argument("--layer", type=int, default=0, metavar="D_MODEL",
+                    help="time the whole layer (projections + path) with this d_model instead")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 counters), if present")
     args = ap.parse_args()
@@ -118,9 +124,13 @@ def main():
     import selective_state_space_depthwise_amd as axon
 
     w = workloads.workload(args.workload)
+    if args.layer:
+        bench_layer(args, w)
+        return
     if w.kind == "decode":
         bench_decode(args, w)
         return
+    variant = {"conv_activation": args.conv_activation, "discretization": args.discretization}
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     adt = torch.bfloat16 if w.act == "bf16" else torch.float32
@@ -147,7 +157,7 @@ def main():
         axon.prefill(s["x"], s["z"], s["dt_raw"], s["B"], s["C"], prm["A_log"], prm["D"],
                      prm["dt_bias"], prm["conv_w"], prm["conv_b"], dt_min=inp0["dt_min"],
                      dt_max=inp0["dt_max"], y=s["y"], conv_cache_out=s["cache"],
-                     ssm_state_out=s["state"], workspace=ws, stream=stream)
+                     ssm_state_out=s["state"], workspace=ws, stream=stream, **variant)
 
     for i in range(args.warmup):
         step(i)
@@ -178,7 +188,8 @@ def main():
         with open(args.traffic_json) as f:
             tj = json.load(f)
         entry = tj.get(w.name)
-        if entry and entry.get("kernel_source_sha") == _kernel_source_sha():
+        default_variant = variant == {"conv_activation": "none", "discretization": "first_order"}
+        if entry and default_variant and entry.get("kernel_source_sha") == _kernel_source_sha():
             traffic = entry.get("bytes_per_launch")
     line = {
         "metric": METRIC,
@@ -195,7 +206,7 @@ def main():
         "data": "synthetic (seeded normal draws, Axon-SSM init for A_log and dt bias)",
         "config": {"workload": w.name, "batch": Bsz, "seq_len": L, "d_inner": E,
                    "d_state": N_STATE, "d_conv": K_CONV, "act_dtype": w.act,
-                   "input_sets_rotated": args.rotate},
+                   "input_sets_rotated": args.rotate, **variant},
         "hbm_gbps": round(achieved, 1),
         "pct_hbm_peak": round(100.0 * achieved / HBM_PEAK_GBPS, 2),
         "event_ms": {"mean": round(launch_ms, 5), "min": round(float(ev_ms.min()), 5),
@@ -275,6 +286,74 @@ def bench_decode(args, w):
                      "note": "state and cache (B E (N + 3) fp32) stay in the last-level cache "
                              "between steps"},
     }
+    print(json.dumps(line), flush=True)
+
+
+def bench_layer(args, w):
+    """One step = one forward of the whole layer (input projection, convolution, selection
+    projection, scan and gate, output projection) over the workload's batch and sequence, with
+    random-initialised weights of the Axon-SSM layer configuration (d_model = --layer)."""
+    import torch
+
+    import selective_state_space_depthwise_amd as axon
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    adt = torch.bfloat16 if w.act == "bf16" else torch.float32
+    Dm = args.layer
+    inp = workloads.layer_inputs(w, Dm)
+    d = {k: torch.from_numpy(inp[k]).to(dev).to(adt) for k in ("x_in", "W_in", "W_f", "W_out")}
+    d.update({k: torch.from_numpy(inp[k]).to(dev) for k in ("A_log", "D", "dt_bias", "conv_w",
+                                                            "conv_b")})
+    Bsz, L, E = w.batch, w.seqlen, w.d_inner
+    out = torch.empty_like(d["x_in"])
+    cache = torch.empty((Bsz, K_CONV - 1, E), dtype=torch.float32, device=dev)
+    state = torch.empty((Bsz, E, N_STATE), dtype=torch.float32, device=dev)
+    layer = axon.Layer()
+    stream = torch.cuda.current_stream(dev)
+    variant = {"conv_activation": args.conv_activation, "discretization": args.discretization}
+
+    def step():
+        layer.forward(d["x_in"], d["W_in"], d["W_f"], d["W_out"], d["A_log"], d["D"],
+                      d["dt_bias"], d["conv_w"], d["conv_b"], dt_min=inp["dt_min"],
+                      dt_max=inp["dt_max"], out=out, conv_cache_out=cache, ssm_state_out=state,
+                      stream=stream, **variant)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    M = Bsz * L
+    flops = 2.0 * M * (2 * E * Dm + (2 * N_STATE + E) * E + Dm * E)
+    launch_ms = float(ev_ms.mean())
+    tflops = flops / (launch_ms / 1e3) / 1e12
+    peak = 2500.0 if w.act == "bf16" else 157.3
+    ms_per_step = wall * 1e3 / args.steps
+    line = {
+        "metric": "Axon-SSM layer forward tokens/s (projections + selective-scan path)",
+        "value": round(M / (ms_per_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.act,
+        "data": "synthetic (seeded normal draws, random-initialised projection weights)",
+        "config": {"workload": w.name + "_layer", "batch": Bsz, "seq_len": L, "d_model": Dm,
+                   "d_inner": E, "d_state": N_STATE, "d_conv": K_CONV, **variant},
+        "event_ms": {"mean": round(launch_ms, 5), "min": round(float(ev_ms.min()), 5),
+                     "median": round(float(np.median(ev_ms)), 5)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None,
+                     "flops_per_launch": flops,
+                     "note": "projection GEMM flops over the whole layer's time"},
+    }
+    layer.close()
     print(json.dumps(line), flush=True)
 
 

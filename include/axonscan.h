@@ -150,6 +150,60 @@ axon_status axon_ssm_decode_step(const axon_ssm_shape* shape, const axon_ssm_par
                                  float* conv_cache, float* ssm_state,
                                  void* y, void* stream);
 
+/* ---- The layer around the path ---------------------------------------------------------------
+ * The whole Axon-SSM layer on (B, L, D) activations [AXON "Gating", "Selective mechanism",
+ * "Code mapping"]:
+ *   (x_branch, z_branch) = split(W_in x)                  W_in (2E, D): rows 0..E-1 give x_branch
+ *   u = conv(x_branch) (+ SiLU with AXON_CONV_SILU)        causal depthwise, K = 4, with the cache
+ *   (B_t, C_t, dt_raw_t) = f_proj(u_t)                    W_f (2N + E, E): rows 0..N-1 give B_t,
+ *                                                           N..2N-1 C_t, 2N..2N+E-1 dt_raw_t
+ *   y = the selective scan of u with B, C, dt_raw, gated by SiLU(z_branch) (as axon_ssm_prefill)
+ *   out = W_out y                                         W_out (D, E)
+ * READING: f_proj is one full-rank linear map from the E conv outputs to [B, C, dt_raw] (the page
+ * states a linear projection and no rank bottleneck), with no bias.
+ * The projections are dense GEMMs (hipBLASLt, fp32 accumulation) in the activation dtype; every
+ * intermediate (x_branch, z_branch, u, B, C, dt_raw, y) is stored in the activation dtype, the
+ * conv cache and the state in fp32. seqlen = 1 with in-place caches is the layer's decode step.
+ *
+ * A context owns the GEMM library handle and its cached GEMM plans; create one per thread (a
+ * context is not safe for concurrent use). The forward call allocates nothing: all scratch is
+ * the caller's workspace. */
+typedef struct axon_layer_ctx axon_layer_ctx;
+
+typedef struct {
+  int64_t batch;      /* B */
+  int64_t seqlen;     /* L >= 1 */
+  int64_t d_model;    /* D */
+  int64_t d_inner;    /* E */
+  int64_t d_state;    /* N, must be 16 */
+  int64_t d_conv;     /* K, must be 4 */
+  axon_dtype act_dtype;  /* x_in, out, the three projection weights and the intermediates */
+} axon_layer_shape;
+
+typedef struct {
+  const void* W_in;   /* (2E, D) activation dtype, row-major (output feature major) */
+  const void* W_f;    /* (2N + E, E) activation dtype */
+  const void* W_out;  /* (D, E) activation dtype */
+  axon_ssm_params ssm;  /* A_log, D, dt_bias, conv_w, conv_b (fp32), dt clips, variants */
+} axon_layer_weights;
+
+/* Create / destroy a context (AXON_ERR_HIP if the GEMM library cannot be initialised). */
+axon_status axon_layer_create(axon_layer_ctx** ctx);
+void axon_layer_destroy(axon_layer_ctx* ctx);
+
+/* Bytes of device workspace axon_layer_forward needs (0 for an invalid shape). */
+size_t axon_layer_workspace_bytes(const axon_layer_shape* shape);
+
+/* Forward over seqlen tokens: x_in (B, L, D) -> out (B, L, D), continuing from the caches as
+ * axon_ssm_prefill does (NULL inputs = zeros; outputs may equal the inputs, in place). out must
+ * not overlap any input, weight or cache; workspace: axon_layer_workspace_bytes(shape) bytes,
+ * 16-byte aligned, contents need no initialisation. */
+axon_status axon_layer_forward(axon_layer_ctx* ctx, const axon_layer_shape* shape,
+                               const axon_layer_weights* weights, const void* x_in,
+                               const float* conv_cache_in, const float* ssm_state_in, void* out,
+                               float* conv_cache_out, float* ssm_state_out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -210,3 +210,64 @@ def decode_step(step: dict, params: dict, conv_cache, ssm_state, threads: int = 
     if rc != 0:
         raise ValueError("oracle_ssm_decode_step rejected its arguments")
     return y
+
+
+# ---- the layer around the path -----------------------------------------------------------------
+def store_as(a, act: str) -> np.ndarray:
+    """Round values to how the GPU path stores an intermediate: float32, or bfloat16 (round to
+    nearest, ties to even), returned as float32."""
+    a32 = np.ascontiguousarray(np.asarray(a, np.float64).astype(np.float32))
+    if act == "bf16":
+        u = a32.view(np.uint32)
+        u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+        a32 = u.view(np.float32)
+    return a32
+
+
+def layer_forward(x_in, W_in, W_f, W_out, params: dict, conv_cache_in=None, ssm_state_in=None,
+                  act: str = "f32", threads: int = 1, lib=None) -> dict:
+    """The whole layer ["Axon-SSM: ...", "Gating", "Selective mechanism", "Code mapping"]:
+      (x_branch, z) = split(W_in x)
+      u = conv(x_branch) with the cache (SiLU after it for the Mamba-block variant)
+      (B_t, C_t, dt_raw_t) = f_proj(u_t), f_proj = W_f (2N + E, E), rows B, C, dt_raw
+      y = the path's scan and gate (``prefill`` on u through an identity convolution)
+      out = W_out y
+    READING: f_proj is one full-rank linear map with no bias. Every product is taken in float64;
+    each intermediate is then stored as the GPU path stores it (``act``: float32 or bfloat16).
+    Returns out (B, L, D) float64, conv_cache (B, K-1, E), ssm_state (B, E, N), and the stored
+    intermediates (x_branch, z, u, B, C, dt_raw, y)."""
+    X = np.asarray(x_in, np.float64)
+    Win = np.asarray(W_in, np.float64)
+    Wf = np.asarray(W_f, np.float64)
+    Wout = np.asarray(W_out, np.float64)
+    Bsz, L, _ = X.shape
+    E = Win.shape[0] // 2
+    N = (Wf.shape[0] - E) // 2
+    K = np.asarray(params["conv_w"]).shape[1]
+    xb = store_as(X @ Win[:E].T, act)
+    z = store_as(X @ Win[E:].T, act)
+    cache = np.zeros((Bsz, K - 1, E)) if conv_cache_in is None else np.asarray(conv_cache_in,
+                                                                               np.float64)
+    full = np.concatenate([cache, xb.astype(np.float64)], axis=1)  # (B, K-1+L, E)
+    w = np.asarray(params["conv_w"], np.float64)
+    v = np.asarray(params["conv_b"], np.float64)[None, None, :] + sum(
+        w[None, None, :, k] * full[:, k:k + L, :] for k in range(K))
+    if params.get("conv_activation", "none") == "silu":
+        v = v / (1.0 + np.exp(-v))
+    u = store_as(v, act)
+    U = u.astype(np.float64)
+    Bm = store_as(U @ Wf[:N].T, act)
+    Cm = store_as(U @ Wf[N:2 * N].T, act)
+    dtr = store_as(U @ Wf[2 * N:].T, act)
+    ident = np.zeros((E, K), np.float32)
+    ident[:, K - 1] = 1.0
+    scan_in = {"x": u, "z": z, "dt_raw": dtr, "B": Bm, "C": Cm, "A_log": params["A_log"],
+               "D": params["D"], "dt_bias": params["dt_bias"], "conv_w": ident,
+               "conv_b": np.zeros(E, np.float32), "dt_min": params["dt_min"],
+               "dt_max": params["dt_max"],
+               "discretization": params.get("discretization", "first_order")}
+    r = prefill(scan_in, ssm_state_in=ssm_state_in, threads=threads, lib=lib)
+    y = store_as(r["y"], act)
+    out = y.astype(np.float64) @ Wout.T
+    return {"out": out, "conv_cache": full[:, -(K - 1):, :].copy(), "ssm_state": r["ssm_state"],
+            "x_branch": xb, "z": z, "u": u, "B": Bm, "C": Cm, "dt_raw": dtr, "y": y}

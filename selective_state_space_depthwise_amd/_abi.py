@@ -44,6 +44,17 @@ class Params(ctypes.Structure):
                 ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float),
                 ("conv_activation", ctypes.c_int32), ("discretization", ctypes.c_int32)]
 
+class LayerShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("d_model", ctypes.c_int64),
+                ("d_inner", ctypes.c_int64), ("d_state", ctypes.c_int64),
+                ("d_conv", ctypes.c_int64), ("act_dtype", ctypes.c_int)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [("W_in", ctypes.c_void_p), ("W_f", ctypes.c_void_p), ("W_out", ctypes.c_void_p),
+                ("ssm", Params)]
+
+
 CONV_ACTIVATIONS = {"none": 0, "silu": 1}
 DISCRETIZATIONS = {"first_order": 0, "zoh": 1}
 
@@ -77,6 +88,16 @@ def load():
         lib.axon_ssm_decode_step.restype = ctypes.c_int
         lib.axon_ssm_decode_step.argtypes = [
             ctypes.POINTER(Shape), ctypes.POINTER(Params), P, P, P, P, P, P, P, P, P]
+        lib.axon_layer_create.restype = ctypes.c_int
+        lib.axon_layer_create.argtypes = [ctypes.POINTER(P)]
+        lib.axon_layer_destroy.restype = None
+        lib.axon_layer_destroy.argtypes = [P]
+        lib.axon_layer_workspace_bytes.restype = ctypes.c_size_t
+        lib.axon_layer_workspace_bytes.argtypes = [ctypes.POINTER(LayerShape)]
+        lib.axon_layer_forward.restype = ctypes.c_int
+        lib.axon_layer_forward.argtypes = [
+            P, ctypes.POINTER(LayerShape), ctypes.POINTER(LayerWeights), P, P, P, P, P, P, P,
+            ctypes.c_size_t, P]
         _lib = lib
         return lib
 
@@ -120,6 +141,37 @@ def raw_decode_step(shape: Shape, params: Params, x, z, dt_raw, B, C, cache, sta
     """axon_ssm_decode_step with integer pointers. Returns the status code."""
     return load().axon_ssm_decode_step(ctypes.byref(shape), ctypes.byref(params), x, z, dt_raw,
                                        B, C, cache, state, y, stream)
+
+
+def make_layer_shape(batch, seqlen, d_model, d_inner, act_bf16, d_state=16,
+                     d_conv=4) -> LayerShape:
+    return LayerShape(int(batch), int(seqlen), int(d_model), int(d_inner), int(d_state),
+                      int(d_conv), AXON_BF16 if act_bf16 else AXON_F32)
+
+
+def layer_workspace_bytes(shape: LayerShape) -> int:
+    return int(load().axon_layer_workspace_bytes(ctypes.byref(shape)))
+
+
+def layer_create() -> int:
+    """A new layer context (an opaque pointer as int); raises AxonError on failure."""
+    h = ctypes.c_void_p()
+    st = load().axon_layer_create(ctypes.byref(h))
+    if st != AXON_OK:
+        raise AxonError(st, "axon_layer_create")
+    return h.value
+
+
+def layer_destroy(ctx: int) -> None:
+    load().axon_layer_destroy(ctx)
+
+
+def raw_layer_forward(ctx, shape: LayerShape, weights: LayerWeights, x_in, cache_in, state_in,
+                      out, cache_out, state_out, workspace, workspace_bytes_, stream) -> int:
+    """axon_layer_forward with integer pointers. Returns the status code."""
+    return load().axon_layer_forward(ctx, ctypes.byref(shape), ctypes.byref(weights), x_in,
+                                     cache_in, state_in, out, cache_out, state_out, workspace,
+                                     int(workspace_bytes_), stream)
 
 
 def declared_functions() -> list[str]:

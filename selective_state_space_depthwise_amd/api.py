@@ -146,4 +146,73 @@ def decode_step(x, z, dt_raw, B, C, A_log, D, dt_bias, conv_w, conv_b, conv_cach
     return y
 
 
-__all__ = ["prefill", "decode_step", "prefill_workspace_bytes", "AxonError"]
+__all__ = ["prefill", "decode_step", "prefill_workspace_bytes", "AxonError", "Layer"]
+
+
+class Layer:
+    """The whole layer on the GPU: out = W_out (scan(conv(W_in_x x), f_proj(u)) * SiLU(W_in_z x)),
+    as axon_layer_forward defines it. Holds a library context (GEMM handle and plans) and a
+    cached workspace tensor; not safe for concurrent use."""
+
+    def __init__(self):
+        self._ctx = _abi.layer_create()
+        self._ws = None
+
+    def close(self):
+        if self._ctx:
+            _abi.layer_destroy(self._ctx)
+            self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 (interpreter shutdown)
+            pass
+
+    def forward(self, x_in, W_in, W_f, W_out, A_log, D, dt_bias, conv_w, conv_b, *,
+                dt_min=1e-4, dt_max=100.0, conv_cache_in=None, ssm_state_in=None, out=None,
+                conv_cache_out=None, ssm_state_out=None, stream=None, conv_activation="none",
+                discretization="first_order"):
+        """x_in (B, L, D) and the weights W_in (2E, D), W_f (2N + E, E), W_out (D, E) in one
+        activation dtype (float32 or bfloat16); the SSM parameters as for ``prefill``.
+        Returns (out, conv_cache, ssm_state)."""
+        device = x_in.device
+        if device.type != "cuda":
+            raise ValueError("Layer.forward runs on the GPU only")
+        bf16 = _act_dtype(x_in)
+        if x_in.dim() != 3:
+            raise ValueError("x_in must be (batch, seqlen, d_model)")
+        Bsz, L, Dm = x_in.shape
+        E = A_log.shape[0]
+        _check(x_in, "x_in", (Bsz, L, Dm), x_in.dtype, device)
+        _check(W_in, "W_in", (2 * E, Dm), x_in.dtype, device)
+        _check(W_f, "W_f", (2 * D_STATE + E, E), x_in.dtype, device)
+        _check(W_out, "W_out", (Dm, E), x_in.dtype, device)
+        prm = _params(A_log, D, dt_bias, conv_w, conv_b, dt_min, dt_max, E, device,
+                      conv_activation, discretization)
+        shape = _abi.make_layer_shape(Bsz, L, Dm, E, bf16)
+        weights = _abi.LayerWeights(W_in.data_ptr(), W_f.data_ptr(), W_out.data_ptr(), prm)
+        if out is None:
+            out = torch.empty_like(x_in)
+        _check(out, "out", (Bsz, L, Dm), x_in.dtype, device)
+        if conv_cache_out is None:
+            conv_cache_out = torch.empty((Bsz, D_CONV - 1, E), dtype=torch.float32, device=device)
+        if ssm_state_out is None:
+            ssm_state_out = torch.empty((Bsz, E, D_STATE), dtype=torch.float32, device=device)
+        for t, n, shp in ((conv_cache_in, "conv_cache_in", (Bsz, D_CONV - 1, E)),
+                          (ssm_state_in, "ssm_state_in", (Bsz, E, D_STATE)),
+                          (conv_cache_out, "conv_cache_out", (Bsz, D_CONV - 1, E)),
+                          (ssm_state_out, "ssm_state_out", (Bsz, E, D_STATE))):
+            if t is not None:
+                _check(t, n, shp, torch.float32, device)
+        need = _abi.layer_workspace_bytes(shape)
+        if self._ws is None or self._ws.numel() < need or self._ws.device != device:
+            self._ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        ptr = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+        st = _abi.raw_layer_forward(self._ctx, shape, weights, x_in.data_ptr(), ptr(conv_cache_in),
+                                    ptr(ssm_state_in), out.data_ptr(), conv_cache_out.data_ptr(),
+                                    ssm_state_out.data_ptr(), self._ws.data_ptr(), need,
+                                    _stream_handle(device, stream))
+        if st != _abi.AXON_OK:
+            raise AxonError(st, "axon_layer_forward")
+        return out, conv_cache_out, ssm_state_out

@@ -16,9 +16,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libaxonscan.so")
 
-HIP_SOURCES = ["axon_kernels.hip", "axon_rowscan.hip"]
+HIP_SOURCES = ["axon_kernels.hip", "axon_rowscan.hip", "axon_layer.hip"]
 CXX_SOURCES = ["axonscan_api.cpp"]
 ARCH = "gfx950"
+ROCM_LIB = "/opt/rocm/lib"  # hipBLASLt (the layer's projection GEMMs)
 # Packed-FP32 instructions stay off: the compiler would otherwise form v_pk_* FP32 ops on its own.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
              "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-command-line-argument"]
@@ -53,7 +54,8 @@ def build(verbose: bool = False) -> str:
               "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
     tmp = LIB + f".tmp{os.getpid()}"
-    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs,
+          f"-L{ROCM_LIB}", "-lhipblaslt", f"-Wl,-rpath,{ROCM_LIB}"], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -6,6 +6,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "axonscan.h"
+
 namespace axon {
 
 constexpr int kState = 16;  // N, states per channel (the Axon-SSM layer configuration)
@@ -58,6 +60,9 @@ struct DecodeLaunch {
 };
 
 int launch_prefill(const PrefillLaunch& a, const PrefillPlan& plan, void* stream);
+// The C-ABI checks of a parameter block (pointers, alignment, clips, variants).
+axon_status validate_params(const axon_ssm_params* p);
+constexpr int64_t kMaxChannels = int64_t(1) << 23;  // d_inner limit of the prefill kernels
 int launch_row_scan(const PrefillLaunch& a, const PrefillPlan& plan, void* stream);
 int launch_decode(const DecodeLaunch& a, void* stream);
 

@@ -15,7 +15,7 @@ constexpr int64_t kMaxBatch = 65535;      // launch grid y dimension
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 // The prefill kernels address a tile of (32 + 3) tokens x d_inner channels with byte offsets
 // below 2^31 (offset 2^31 marks a masked store).
-constexpr int64_t kMaxDInner = int64_t(1) << 23;
+constexpr int64_t kMaxDInner = axon::kMaxChannels;
 
 // Work split of the prefill (measured on MI355X, 1024 SIMDs):
 //  - from kSinglePassChannels channels, one state per lane (W = 4 waves per 16 channels) gives
@@ -98,6 +98,8 @@ void param_spans(const axon_ssm_params* p, int64_t E, Span out[5]) {
 }  // namespace
 
 namespace axon {
+
+axon_status validate_params(const axon_ssm_params* p) { return check_params(p); }
 
 PrefillPlan plan_prefill(int64_t batch, int64_t seqlen, int64_t d_inner) {
   PrefillPlan plan;

@@ -469,7 +469,93 @@ def pin_variants_decode_equals_prefill(lib=None):
             np.testing.assert_array_equal(state, full["ssm_state"])
 
 
+# ---- the layer around the path ------------------------------------------------------------------
+def _layer_case(seed, Bsz=2, L=13, E=32, act_name="none"):
+    inp, extra = _case(L, E=E, Bsz=Bsz, seed=seed, h0=True, cache=True)
+    inp["conv_activation"] = act_name
+    return inp, extra
+
+
+def pin_layer_reduces_to_path(lib=None, layer=None):
+    """With W_in = [I; I] (D = E), f_proj selecting channels 0..N-1 of u for B, N..2N-1 for C
+    and the identity for dt_raw, and W_out = I, the layer is the path itself on x = z = x_in with
+    B, C, dt_raw read off the convolution output: the order of [AXON "Gating" / "Selective
+    mechanism"] (projection, conv, f_proj from the conv output, scan, gate, output projection)."""
+    layer = layer or oracle.layer_forward
+    for act_name in ("none", "silu"):
+        inp, extra = _layer_case(50, act_name=act_name)
+        Bsz, L, E = inp["x"].shape
+        X = inp["x"].astype(np.float64)
+        W_in = np.concatenate([np.eye(E), np.eye(E)])
+        W_f = np.zeros((2 * N + E, E))
+        W_f[np.arange(N), np.arange(N)] = 1.0
+        W_f[N + np.arange(N), N + np.arange(N)] = 1.0
+        W_f[2 * N:, :] = np.eye(E)
+        r = layer(X, W_in, W_f, np.eye(E), inp, conv_cache_in=extra["conv_cache_in"],
+                  ssm_state_in=extra["ssm_state_in"], lib=lib)
+        # the path directly: u per channel from the oracle's own convolution, then B, C, dt_raw
+        u = np.stack([np.stack([oracle.channel(inp, b, e, **extra)["u"] for e in range(E)], -1)
+                      for b in range(Bsz)])
+        direct = dict(inp)
+        direct.update(z=inp["x"], B=u[..., :N].astype(np.float32),
+                      C=u[..., N:2 * N].astype(np.float32), dt_raw=u.astype(np.float32))
+        ref = oracle.prefill(direct, lib=lib, **extra)
+        np.testing.assert_allclose(r["out"], ref["y"], rtol=2e-6, atol=2e-6)
+        np.testing.assert_allclose(r["ssm_state"], ref["ssm_state"], rtol=2e-6, atol=2e-6)
+        np.testing.assert_array_equal(r["conv_cache"], ref["conv_cache"])
+
+
+def pin_layer_projections(lib=None, layer=None):
+    """The projections are plain matrix products: out is linear in W_out (out(W_out A) =
+    out(W_out) A^T-mixed: here a column permutation and a scale), and the x / z branches are the
+    first / second halves of W_in (swapping the halves of W_in equals swapping x and z)."""
+    layer = layer or oracle.layer_forward
+    g = np.random.default_rng(51)
+    inp, extra = _layer_case(52, E=24)
+    Bsz, L, E = inp["x"].shape
+    Dm = 20
+    X = g.standard_normal((Bsz, L, Dm))
+    W_in = g.standard_normal((2 * E, Dm)) / np.sqrt(Dm)
+    W_f = g.standard_normal((2 * N + E, E)) / np.sqrt(E)
+    W_out = g.standard_normal((Dm, E)) / np.sqrt(E)
+    r = layer(X, W_in, W_f, W_out, inp, lib=lib)
+    perm = g.permutation(Dm)
+    r2 = layer(X, W_in, W_f, 4.0 * W_out[perm], inp, lib=lib)
+    np.testing.assert_allclose(r2["out"], 4.0 * r["out"][..., perm], rtol=1e-12, atol=1e-12)
+    # y = W_out^-1-free check: out = y W_out^T with the stored y
+    np.testing.assert_allclose(r["out"], r["y"].astype(np.float64) @ W_out.T, rtol=1e-12,
+                               atol=1e-12)
+    # branches: x_branch = X W_in[:E]^T, z = X W_in[E:]^T (as stored in float32)
+    np.testing.assert_array_equal(r["x_branch"], (X @ W_in[:E].T).astype(np.float32))
+    np.testing.assert_array_equal(r["z"], (X @ W_in[E:].T).astype(np.float32))
+
+
+def pin_layer_step_equals_prefill(lib=None, layer=None):
+    """The layer one token at a time with its caches equals the layer over all tokens."""
+    layer = layer or oracle.layer_forward
+    g = np.random.default_rng(53)
+    inp, extra = _layer_case(54, E=20, L=9)
+    Bsz, L, E = inp["x"].shape
+    Dm = 12
+    X = g.standard_normal((Bsz, L, Dm))
+    W_in = g.standard_normal((2 * E, Dm)) / np.sqrt(Dm)
+    W_f = g.standard_normal((2 * N + E, E)) / np.sqrt(E)
+    W_out = g.standard_normal((Dm, E)) / np.sqrt(E)
+    full = layer(X, W_in, W_f, W_out, inp, lib=lib, **extra)
+    cache, state = extra["conv_cache_in"], extra["ssm_state_in"]
+    outs = []
+    for t in range(L):
+        r = layer(X[:, t:t + 1], W_in, W_f, W_out, inp, conv_cache_in=cache, ssm_state_in=state,
+                  lib=lib)
+        cache, state = r["conv_cache"], r["ssm_state"]
+        outs.append(r["out"])
+    np.testing.assert_allclose(np.concatenate(outs, axis=1), full["out"], rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(state, full["ssm_state"], rtol=1e-10, atol=1e-10)
+    np.testing.assert_array_equal(cache, full["conv_cache"])
+
+
 ALL_PINS = [
+    pin_layer_reduces_to_path, pin_layer_projections, pin_layer_step_equals_prefill,
     pin_zoh_glossary_worked_example, pin_zoh_lti_closed_form, pin_conv_silu,
     pin_variants_decode_equals_prefill,
     pin_lti_closed_form, pin_glossary_worked_example, pin_zero_input_decay, pin_dt_clip_bounds,

@@ -183,3 +183,45 @@ def test_decode_rejects_bad_arguments():
     assert _decode(y=b["cin"]) == A.AXON_ERR_INVALID_ARGUMENT
     assert _decode(sin=b["cin"]) == A.AXON_ERR_INVALID_ARGUMENT
     assert _decode(params=_params(dt_min=2.0, dt_max=1.0)) == A.AXON_ERR_INVALID_ARGUMENT
+
+
+# ---- the layer entry points (no GPU calls: every case is rejected before any launch) ----------
+def _lshape(**kw):
+    base = dict(batch=1, seqlen=8, d_model=32, d_inner=48, act_bf16=False)
+    base.update(kw)
+    return A.make_layer_shape(base["batch"], base["seqlen"], base["d_model"], base["d_inner"],
+                              base["act_bf16"], d_state=base.get("d_state", 16),
+                              d_conv=base.get("d_conv", 4))
+
+
+def test_layer_workspace_is_a_pure_function_of_shape():
+    a = A.layer_workspace_bytes(_lshape())
+    assert a > 0 and a % 256 == 0 and a == A.layer_workspace_bytes(_lshape())
+    assert A.layer_workspace_bytes(_lshape(seqlen=64)) > a
+    assert A.layer_workspace_bytes(_lshape(d_state=8)) == 0
+    assert A.layer_workspace_bytes(_lshape(seqlen=0)) == 0
+
+
+_FAKE_CTX = ctypes.create_string_buffer(4096)  # zeroed host memory: a context with no handle
+
+
+def _lforward(ctx=ctypes.addressof(_FAKE_CTX), shape=None, params=None, ws_bytes=1 << 32, **over):
+    b = _buffers()
+    b.update(over)
+    w = A.LayerWeights(P + (5 << 30), P + (6 << 30), P + (7 << 30), params or _params())
+    return A.raw_layer_forward(ctx, shape or _lshape(), w, b["x"], b["cin"], b["sin"], b["y"],
+                               b["cout"], b["sout"], b["ws"], ws_bytes, None)
+
+
+def test_layer_forward_rejects_bad_arguments():
+    assert _lforward(ctx=None) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _lforward(shape=_lshape(d_state=8)) == A.AXON_ERR_UNSUPPORTED
+    assert _lforward(shape=_lshape(seqlen=0)) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _lforward(x=P + 4) == A.AXON_ERR_INVALID_ARGUMENT          # misaligned input
+    assert _lforward(y=None) == A.AXON_ERR_INVALID_ARGUMENT           # no output
+    assert _lforward(ws_bytes=16) == A.AXON_ERR_WORKSPACE_TOO_SMALL
+    assert _lforward(y=_buffers()["x"]) == A.AXON_ERR_INVALID_ARGUMENT  # out overlaps x_in
+    bad = A.make_params(*([P + (1 << 30) + i * (1 << 20) for i in range(5)]), 1e-4, 100.0,
+                        conv_activation=3)
+    assert _lforward(params=bad) == A.AXON_ERR_UNSUPPORTED
+    assert _lforward() == A.AXON_ERR_INVALID_ARGUMENT                 # context without a handle

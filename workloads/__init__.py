@@ -165,6 +165,31 @@ def decode_step_inputs(w: Workload, step: int, batch: int | None = None,
     return out
 
 
+TID_XIN, TID_WIN, TID_WF, TID_WOUT = 21, 22, 23, 24
+
+
+def layer_inputs(w: Workload, d_model: int, batch: int | None = None, seqlen: int | None = None,
+                 d_inner: int | None = None) -> dict:
+    """Inputs of the whole layer: x_in (B, L, D) ~ N(0, 1) and random-initialised projection
+    weights W_in (2E, D) ~ N(0, 1/D), W_f (2N + E, E) ~ N(0, 1/E), W_out (D, E) ~ N(0, 1/E),
+    plus the SSM parameters of ``params`` (no trained weights exist here). bf16 workloads
+    round x_in and the three projections to bf16."""
+    Bsz = batch or w.batch
+    L = w.seqlen if seqlen is None else seqlen
+    E = d_inner or w.d_inner
+    seed = w.seed
+    out = params(w, E)
+    out["x_in"] = _normal(seed, TID_XIN, (Bsz, L, d_model))
+    out["W_in"] = _normal(seed, TID_WIN, (2 * E, d_model), scale=d_model ** -0.5)
+    out["W_f"] = _normal(seed, TID_WF, (2 * D_STATE + E, E), scale=E ** -0.5)
+    out["W_out"] = _normal(seed, TID_WOUT, (d_model, E), scale=E ** -0.5)
+    if w.act == "bf16":
+        for k in ("x_in", "W_in", "W_f", "W_out"):
+            out[k] = bf16_round(out[k])
+    out["act"] = w.act
+    return out
+
+
 def workload(name_or_index) -> Workload:
     if isinstance(name_or_index, int):
         return WORKLOADS[name_or_index]
