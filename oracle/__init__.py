@@ -271,3 +271,34 @@ def layer_forward(x_in, W_in, W_f, W_out, params: dict, conv_cache_in=None, ssm_
     out = y.astype(np.float64) @ Wout.T
     return {"out": out, "conv_cache": full[:, -(K - 1):, :].copy(), "ssm_state": r["ssm_state"],
             "x_branch": xb, "z": z, "u": u, "B": Bm, "C": Cm, "dt_raw": dtr, "y": y}
+
+
+# ---- Mamba-2 SSD core ----------------------------------------------------------------------------
+def ssd_scan(inp: dict, state_in=None, threads: int = 1, lib=None) -> dict:
+    """The SSD core over x (B, L, H, P), dt_raw (B, L, H), B, C (B, L, N) float32 with A_log,
+    D, dt_bias (H,) and the dt clips (see oracle_ssd_scan). Returns y (B, L, H, P) and
+    ssm_state (B, H, P, N), float64."""
+    lib = _load(lib)
+    if not hasattr(lib, "_ssd_declared"):
+        P_, I_, D_ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double
+        lib.oracle_ssd_scan.restype = ctypes.c_int
+        lib.oracle_ssd_scan.argtypes = [I_, I_, I_, I_, I_, P_, P_, P_, P_, P_, P_, P_, D_, D_,
+                                        P_, P_, P_, ctypes.c_int]
+        lib._ssd_declared = True
+    x, dtr = _f32(inp["x"]), _f32(inp["dt_raw"])
+    Bm, Cm = _f32(inp["B"]), _f32(inp["C"])
+    Bsz, L, H, P = x.shape
+    N = Bm.shape[2]
+    assert dtr.shape == (Bsz, L, H) and Bm.shape == (Bsz, L, N) and Cm.shape == (Bsz, L, N)
+    sin = _f64(state_in)
+    if sin is not None:
+        assert sin.shape == (Bsz, H, P, N)
+    y = np.empty((Bsz, L, H, P), np.float64)
+    sout = np.empty((Bsz, H, P, N), np.float64)
+    rc = lib.oracle_ssd_scan(Bsz, L, H, P, N, _ptr(x), _ptr(dtr), _ptr(Bm), _ptr(Cm),
+                             _ptr(_f32(inp["A_log"])), _ptr(_f32(inp["D"])),
+                             _ptr(_f32(inp["dt_bias"])), float(inp["dt_min"]),
+                             float(inp["dt_max"]), _ptr(sin), _ptr(y), _ptr(sout), int(threads))
+    if rc != 0:
+        raise ValueError("oracle_ssd_scan rejected its arguments")
+    return {"y": y, "ssm_state": sout}

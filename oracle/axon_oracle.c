@@ -224,3 +224,88 @@ int oracle_ssm_decode_step(int64_t Bsz, int64_t E, int64_t N, int64_t K,
                             conv_cache,
                             ssm_state, NULL, threads);
 }
+
+/* ---- Mamba-2 SSD core -------------------------------------------------------------------------
+ * ["Selective State Space Models (Mamba)", pattern "Mamba-2 block": d_state 128, headdim 64;
+ * the SSD article: the same selective recurrence with one scalar decay per head, which makes it
+ * a masked linear attention]. Plain sequential recurrence, one (b, head) at a time.
+ * READING: first-order input term dt B (as the Axon-SSM layer), B and C shared by all heads
+ * (one group), no convolution and no gate (those belong to the block around the core). */
+typedef struct {
+  int64_t Bsz, L, H, P, N;
+  const float *x, *dt_raw, *Bm, *Cm, *A_log, *D, *dt_bias;
+  double dt_min, dt_max;
+  const double* state_in;
+  double *y, *state_out;
+  int64_t begin, end; /* (b, head) index range */
+  int status;
+} ssd_job;
+
+static void* ssd_worker(void* arg) {
+  ssd_job* j = (ssd_job*)arg;
+  const int64_t L = j->L, H = j->H, P = j->P, N = j->N;
+  double* h = (double*)malloc(sizeof(double) * (size_t)(P * N));
+  if (!h) { j->status = -1; return NULL; }
+  j->status = 0;
+  for (int64_t bh = j->begin; bh < j->end; ++bh) {
+    const int64_t b = bh / H, hd = bh % H;
+    const double A = -exp((double)j->A_log[hd]);
+    for (int64_t i = 0; i < P * N; ++i) h[i] = j->state_in ? j->state_in[bh * P * N + i] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+      double dt = softplus((double)j->dt_raw[(b * L + t) * H + hd] + (double)j->dt_bias[hd]);
+      if (dt < j->dt_min) dt = j->dt_min;
+      if (dt > j->dt_max) dt = j->dt_max;
+      const double a = exp(dt * A);
+      const float* xt = j->x + ((b * L + t) * H + hd) * P;
+      const float* Bt = j->Bm + (b * L + t) * N;
+      const float* Ct = j->Cm + (b * L + t) * N;
+      double* yt = j->y + ((b * L + t) * H + hd) * P;
+      for (int64_t p = 0; p < P; ++p) {
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          h[p * N + n] = a * h[p * N + n] + dt * (double)xt[p] * (double)Bt[n];
+          acc += (double)Ct[n] * h[p * N + n];
+        }
+        yt[p] = acc + (double)j->D[hd] * (double)xt[p];
+      }
+    }
+    for (int64_t i = 0; i < P * N; ++i) j->state_out[bh * P * N + i] = h[i];
+  }
+  free(h);
+  return NULL;
+}
+
+int oracle_ssd_scan(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N,
+                    const float* x, const float* dt_raw, const float* Bm, const float* Cm,
+                    const float* A_log, const float* D, const float* dt_bias, double dt_min,
+                    double dt_max, const double* state_in, double* y, double* state_out,
+                    int threads) {
+  if (Bsz < 1 || L < 0 || H < 1 || P < 1 || N < 1 || !A_log || !D || !dt_bias || !state_out)
+    return -1;
+  if (L > 0 && (!x || !dt_raw || !Bm || !Cm || !y)) return -1;
+  const int64_t total = Bsz * H;
+  if (threads < 1) threads = 1;
+  if (threads > 256) threads = 256;
+  if ((int64_t)threads > total) threads = (int)total;
+  ssd_job jobs[256];
+  pthread_t tids[256];
+  int started[256];
+  for (int i = 0; i < threads; ++i) {
+    ssd_job jb = {Bsz, L, H, P, N, x, dt_raw, Bm, Cm, A_log, D, dt_bias, dt_min, dt_max,
+                  state_in, y, state_out, total * i / threads, total * (i + 1) / threads, 0};
+    jobs[i] = jb;
+    started[i] = 0;
+  }
+  for (int i = 1; i < threads; ++i)
+    started[i] = pthread_create(&tids[i], NULL, ssd_worker, &jobs[i]) == 0;
+  ssd_worker(&jobs[0]);
+  int status = jobs[0].status;
+  for (int i = 1; i < threads; ++i) {
+    if (started[i])
+      pthread_join(tids[i], NULL);
+    else
+      ssd_worker(&jobs[i]);
+    if (jobs[i].status != 0) status = jobs[i].status;
+  }
+  return status;
+}

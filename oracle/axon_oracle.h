@@ -82,3 +82,24 @@ int oracle_ssm_decode_step(int64_t Bsz, int64_t E, int64_t N, int64_t K,
 #endif
 
 #endif /* AXON_ORACLE_H_ */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Mamba-2 state space duality (SSD) core, per batch row b and head hd (a further layer the pages
+ * describe: "Selective State Space Models (Mamba)", pattern "Mamba-2 block"; the SSD article):
+ *   dt_t = clip(softplus(dt_raw_t + dt_bias), dt_min, dt_max),  A = -exp(A_log)  (one scalar)
+ *   h_t[p, n] = exp(dt_t A) h_{t-1}[p, n] + dt_t x_t[p] B_t[n]
+ *   y_t[p]    = sum_n C_t[n] h_t[p, n] + D x_t[p]
+ * x, y (B, L, H, P); dt_raw (B, L, H); Bm, Cm (B, L, N) shared by all heads; A_log, D, dt_bias
+ * (H); state_in / state_out (B, H, P, N) (state_in NULL = zeros). Returns 0 or -1. */
+int oracle_ssd_scan(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N,
+                    const float* x, const float* dt_raw, const float* Bm, const float* Cm,
+                    const float* A_log, const float* D, const float* dt_bias, double dt_min,
+                    double dt_max, const double* state_in, double* y, double* state_out,
+                    int threads);
+
+#ifdef __cplusplus
+}
+#endif

@@ -554,7 +554,97 @@ def pin_layer_step_equals_prefill(lib=None, layer=None):
     np.testing.assert_array_equal(cache, full["conv_cache"])
 
 
+# ---- Mamba-2 SSD core ----------------------------------------------------------------------------
+def _ssd_case(seed, Bsz=2, L=23, H=3, P=5, Nn=7, h0=True):
+    g = np.random.default_rng(seed)
+    f = lambda *s: g.standard_normal(s).astype(np.float32)  # noqa: E731
+    inp = {"x": f(Bsz, L, H, P), "dt_raw": f(Bsz, L, H), "B": f(Bsz, L, Nn), "C": f(Bsz, L, Nn),
+           "A_log": g.uniform(-1.0, 1.5, H).astype(np.float32), "D": f(H),
+           "dt_bias": g.uniform(-3.0, 0.0, H).astype(np.float32), "dt_min": 1e-4,
+           "dt_max": 100.0}
+    state = g.standard_normal((Bsz, H, P, Nn)) if h0 else None
+    return inp, state
+
+
+def _ssd_dt(inp):
+    v = inp["dt_raw"].astype(np.float64) + inp["dt_bias"].astype(np.float64)
+    return np.clip(np.logaddexp(0.0, v), inp["dt_min"], inp["dt_max"])
+
+
+def pin_ssd_masked_matrix_form(lib=None):
+    """State space duality [WIKI "Mamba-2 block"; the SSD article, "State space duality"]: the
+    recurrence with a scalar decay per head equals a masked linear attention,
+        y = (Lmask o (C B^T)) (dt x) + D x + exp(cum) (C h0^T),
+    Lmask[t, s] = exp(cum_t - cum_s) for s <= t else 0, cum_t = sum_{r<=t} dt_r A. The final
+    state is sum_s exp(cum_L - cum_s) dt_s x_s B_s^T + exp(cum_L) h0. Checked in float64 with
+    numpy matrix products."""
+    inp, h0 = _ssd_case(60)
+    r = oracle.ssd_scan(inp, state_in=h0, lib=lib)
+    Bsz, L, H, P = inp["x"].shape
+    dt = _ssd_dt(inp)
+    A = -np.exp(inp["A_log"].astype(np.float64))
+    for b in range(Bsz):
+        G = inp["C"][b].astype(np.float64) @ inp["B"][b].astype(np.float64).T  # (L, L)
+        for hd in range(H):
+            cum = np.cumsum(dt[b, :, hd] * A[hd])
+            mask = np.tril(np.exp(cum[:, None] - cum[None, :]))
+            X = inp["x"][b, :, hd].astype(np.float64)
+            y = (mask * G) @ (dt[b, :, hd, None] * X) + inp["D"][hd] * X
+            y += np.exp(cum)[:, None] * (inp["C"][b].astype(np.float64) @ h0[b, hd].T)
+            np.testing.assert_allclose(r["y"][b, :, hd], y, rtol=1e-10, atol=1e-10)
+            w = np.exp(cum[-1] - cum) * dt[b, :, hd]
+            hL = (w[:, None] * X).T @ inp["B"][b].astype(np.float64) + np.exp(cum[-1]) * h0[b, hd]
+            np.testing.assert_allclose(r["ssm_state"][b, hd], hL, rtol=1e-10, atol=1e-10)
+
+
+def pin_ssd_reduces_to_axon(lib=None):
+    """A head of headdim P is P channels that share one decay rate: with A_log[e, n] = A_log[h]
+    for every state n, dt_raw, dt_bias and D broadcast over the head's channels, an identity
+    convolution (tap K-1 = 1, no bias) and the gate divided out, the Axon-SSM path over
+    E = H * P channels (already pinned) gives the SSD core's outputs and states."""
+    Nn = N
+    inp, _ = _ssd_case(61, Bsz=2, L=19, H=3, P=4, Nn=Nn, h0=False)
+    Bsz, L, H, P = inp["x"].shape
+    E = H * P
+    g = np.random.default_rng(62)
+    h0 = g.standard_normal((Bsz, H, P, Nn))
+    z = np.full((Bsz, L, E), 2.5, np.float32)
+    ax = {"x": inp["x"].reshape(Bsz, L, E), "z": z,
+          "dt_raw": np.repeat(inp["dt_raw"], P, axis=2), "B": inp["B"], "C": inp["C"],
+          "A_log": np.repeat(inp["A_log"], P)[:, None].repeat(Nn, 1).astype(np.float32),
+          "D": np.repeat(inp["D"], P), "dt_bias": np.repeat(inp["dt_bias"], P),
+          "conv_w": np.tile(np.array([0, 0, 0, 1], np.float32), (E, 1)),
+          "conv_b": np.zeros(E, np.float32), "dt_min": inp["dt_min"], "dt_max": inp["dt_max"]}
+    ref = oracle.prefill(ax, ssm_state_in=h0.reshape(Bsz, E, Nn), lib=lib)
+    r = oracle.ssd_scan(inp, state_in=h0, lib=lib)
+    gate = float(_silu(2.5))
+    np.testing.assert_allclose(r["y"].reshape(Bsz, L, E), ref["y"] / gate, rtol=1e-9, atol=1e-9)
+    np.testing.assert_allclose(r["ssm_state"].reshape(Bsz, E, Nn), ref["ssm_state"], rtol=1e-12,
+                               atol=1e-12)
+
+
+def pin_ssd_continuation_and_empty(lib=None):
+    """Running L1 tokens and then L2 from the returned state equals running L1 + L2; an empty
+    sequence returns the incoming state unchanged."""
+    inp, h0 = _ssd_case(63, L=17)
+    L1 = 6
+    full = oracle.ssd_scan(inp, state_in=h0, lib=lib)
+    part = lambda a, b: {k: (v[:, a:b] if isinstance(v, np.ndarray) and v.ndim >= 3 else v)  # noqa
+                         for k, v in inp.items()}
+    r1 = oracle.ssd_scan(part(0, L1), state_in=h0, lib=lib)
+    r2 = oracle.ssd_scan(part(L1, None), state_in=r1["ssm_state"], lib=lib)
+    np.testing.assert_allclose(np.concatenate([r1["y"], r2["y"]], 1), full["y"], rtol=1e-12,
+                               atol=1e-12)
+    np.testing.assert_allclose(r2["ssm_state"], full["ssm_state"], rtol=1e-12, atol=1e-12)
+    e = oracle.ssd_scan(part(0, 0), state_in=h0, lib=lib)
+    assert e["y"].shape[1] == 0
+    np.testing.assert_array_equal(e["ssm_state"], h0)
+    z = oracle.ssd_scan(part(0, 0), lib=lib)
+    np.testing.assert_array_equal(z["ssm_state"], np.zeros_like(h0))
+
+
 ALL_PINS = [
+    pin_ssd_masked_matrix_form, pin_ssd_reduces_to_axon, pin_ssd_continuation_and_empty,
     pin_layer_reduces_to_path, pin_layer_projections, pin_layer_step_equals_prefill,
     pin_zoh_glossary_worked_example, pin_zoh_lti_closed_form, pin_conv_silu,
     pin_variants_decode_equals_prefill,

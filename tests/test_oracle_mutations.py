@@ -44,6 +44,21 @@ MUTATIONS = {
     "no_lower_clip": ("if (dt < dt_min) dt = dt_min;", ""),
     "gate_sigmoid_not_silu": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
     "D_times_x_not_u": ("acc += D * u;", "acc += D * xt;"),
+    "ssd_readout_before_update": (
+        "          h[p * N + n] = a * h[p * N + n] + dt * (double)xt[p] * (double)Bt[n];\n"
+        "          acc += (double)Ct[n] * h[p * N + n];",
+        "          acc += (double)Ct[n] * h[p * N + n];\n"
+        "          h[p * N + n] = a * h[p * N + n] + dt * (double)xt[p] * (double)Bt[n];"),
+    "ssd_B_C_swapped": ("dt * (double)xt[p] * (double)Bt[n];", "dt * (double)xt[p] * (double)Ct[n];"),
+    "ssd_D_dropped": ("yt[p] = acc + (double)j->D[hd] * (double)xt[p];", "yt[p] = acc;"),
+    "ssd_A_of_head0": ("const double A = -exp((double)j->A_log[hd]);",
+                       "const double A = -exp((double)j->A_log[0]);"),
+    "ssd_dt_of_head0": ("softplus((double)j->dt_raw[(b * L + t) * H + hd]",
+                        "softplus((double)j->dt_raw[(b * L + t) * H]"),
+    "ssd_state_transposed": ("h[p * N + n] = a * h[p * N + n]", "h[p * N + n] = a * h[n * P + p]"),
+    "ssd_decay_without_dt": ("const double a = exp(dt * A);", "const double a = exp(A);"),
+    "ssd_state_in_ignored": ("h[i] = j->state_in ? j->state_in[bh * P * N + i] : 0.0;",
+                             "h[i] = 0.0;"),
     "state_in_ignored": ("h[n] = h_in ? h_in[n] : 0.0;", "h[n] = 0.0;"),
 }
 
