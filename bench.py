@@ -106,6 +106,8 @@ def main():
                     help="variant: exact zero-order hold")
     ap.add_argument("--layer", type=int, default=0, metavar="D_MODEL",
                     help="time the whole layer (projections + path) with this d_model instead")
+    ap.add_argument("--ssd", default="", metavar="WORKLOAD",
+                    help="time the Mamba-2 SSD core instead (e.g. mamba2_ssd_f32_b1_l2048_h64)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 counters), if present")
     args = ap.parse_args()
@@ -123,6 +125,9 @@ def main():
 
     import selective_state_space_depthwise_amd as axon
 
+    if args.ssd:
+        bench_ssd(args, next(x for x in workloads.SSD_WORKLOADS if x.name == args.ssd))
+        return
     w = workloads.workload(args.workload)
     if args.layer:
         bench_layer(args, w)
@@ -357,12 +362,114 @@ def bench_layer(args, w):
     print(json.dumps(line), flush=True)
 
 
+def ssd_algorithmic_flops(Bsz, L, H, P=64, N=128, Q=64):
+    """Multiply-add flops (2 per product) of the chunked SSD form per call: per (batch, chunk)
+    the lower block triangle of C B^T (10 of 16 16x16 blocks over N); per (batch, head, chunk)
+    the chunk state x^T diag(w) B (P x N over Q), the incoming-state readout C H^T (Q x P over
+    N) and the lower block triangle of the masked (C B^T) times x (10 of 16 blocks, over Q)."""
+    nc = -(-L // Q)
+    gram = 10 * 16 * 16 * N * 2
+    per_head = P * N * Q * 2 + Q * P * N * 2 + 10 * 16 * 16 * P * 2
+    return Bsz * nc * (gram + H * per_head)
+
+
+def bench_ssd(args, w):
+    """One step = one axon_ssd_scan call (four kernels: C B^T per chunk, chunk states, the
+    recurrence over chunks, outputs) over the workload's batch, from a zero state."""
+    import torch
+
+    import selective_state_space_depthwise_amd as axon
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    adt = torch.bfloat16 if w.act == "bf16" else torch.float32
+    elt = 2 if w.act == "bf16" else 4
+    Bsz, L, H = w.batch, w.seqlen, w.heads
+    inp0 = workloads.ssd_inputs(w)
+    prm = {k: torch.from_numpy(inp0[k]).to(dev) for k in ("A_log", "D", "dt_bias")}
+    sets = []
+    for r in range(args.rotate):
+        inp = inp0 if r == 0 else workloads.ssd_inputs(w, seed_offset=r)
+        s = {k: torch.from_numpy(inp[k]).to(dev).to(adt) for k in ("x", "dt_raw", "B", "C")}
+        s["y"] = torch.empty_like(s["x"])
+        s["state"] = torch.empty((Bsz, H, 64, 128), dtype=torch.float32, device=dev)
+        sets.append(s)
+    ws = torch.empty(max(axon.ssd_workspace_bytes(Bsz, L, H, w.act == "bf16"), 1),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        s = sets[i % len(sets)]
+        axon.ssd_scan(s["x"], s["dt_raw"], s["B"], s["C"], prm["A_log"], prm["D"],
+                      prm["dt_bias"], dt_min=inp0["dt_min"], dt_max=inp0["dt_max"], y=s["y"],
+                      state_out=s["state"], workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(args.warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    launch_ms = float(ev_ms.mean())
+    flops = ssd_algorithmic_flops(Bsz, L, H)
+    tflops = flops / (launch_ms / 1e3) / 1e12
+    hbm = elt * (2 * Bsz * L * H * 64 + Bsz * L * H + 2 * Bsz * L * 128) + 4 * Bsz * H * 64 * 128
+    ms_per_step = wall * 1e3 / args.steps
+    line = {
+        "metric": "Mamba-2 SSD core tokens/s (64 heads x 64, d_state 128)",
+        "value": round(Bsz * L / (ms_per_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded normal draws, A in [-16, -1], dt in [1e-3, 0.1] + N(0,1) raw)",
+        "config": {"workload": w.name, "batch": Bsz, "seq_len": L, "n_heads": H, "head_dim": 64,
+                   "d_state": 128, "chunk": 64, "act_dtype": w.act,
+                   "input_sets_rotated": args.rotate},
+        "event_ms": {"mean": round(launch_ms, 5), "min": round(float(ev_ms.min()), 5),
+                     "median": round(float(np.median(ev_ms)), 5)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": 157.3,
+                     "unit": "TFLOP/s", "frac": round(tflops / 157.3, 4), "traffic": None,
+                     "flops_per_launch": flops,
+                     "note": "fp32 matrix-core flops of the chunked form over the whole call "
+                             "(four kernels)"},
+        "hbm_gbps_of_call": round(hbm / (launch_ms / 1e3) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = min(16, os.cpu_count() or 1)
+        Ls = 128
+        sample = {k: (v[:, :Ls] if k in ("x", "dt_raw", "B", "C") else v) for k, v in inp0.items()}
+        oracle.ssd_scan({k: (v[:, :4] if k in ("x", "dt_raw", "B", "C") else v)
+                         for k, v in inp0.items()}, threads=threads)
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            oracle.ssd_scan(sample, threads=threads)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= 10.0:
+                break
+        line["cpu_baseline"] = {
+            "value": round(passes * Bsz * Ls / el, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "sample": f"first {Ls} tokens of the workload, all {H} heads, "
+                                        f"{passes} passes in {el:.1f} s, double precision"}
+    print(json.dumps(line), flush=True)
+
+
 def _kernel_source_sha():
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_depthwise_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    # the sources the prefill kernels are built from
+    for name in ("axon_device.h", "axon_internal.h", "axon_kernels.hip", "axon_rowscan.hip",
+                 "axonscan_api.cpp"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]

@@ -204,6 +204,65 @@ axon_status axon_layer_forward(axon_layer_ctx* ctx, const axon_layer_shape* shap
                                float* conv_cache_out, float* ssm_state_out, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* ---- Mamba-2 SSD core ------------------------------------------------------------------------
+ * The state space duality (SSD) layer core of Mamba-2 ["Selective State Space Models (Mamba)",
+ * pattern "Mamba-2 block": d_state 128, headdim 64; the SSD article, sections on the duality
+ * with linear attention and on the chunked scan]. Heads of head_dim P channels share one scalar
+ * decay; for every batch row b and head h, with a state h[p, n] (P x N), for t = 0..L-1:
+ *
+ *   dt_t      = min(max(softplus(dt_raw[b,t,h] + dt_bias[h]), dt_min), dt_max)
+ *   A         = -exp(A_log[h])
+ *   h[p, n]  <- exp(dt_t A) h[p, n] + dt_t x[b,t,h,p] B[b,t,n]
+ *   y[b,t,h,p] = sum_n C[b,t,n] h[p, n] + D[h] x[b,t,h,p]
+ *
+ * READING: the first-order input term dt B and the step size of the Axon-SSM layer; B and C are
+ * shared by all heads (one group); the convolution, gate and projections of the Mamba-2 block
+ * are the caller's. The library computes it in chunks of 64 tokens: within a chunk as matrix
+ * products on the matrix cores (the decay-masked C B^T times dt x, the chunk's state
+ * contribution x^T diag(w) B and the readout of the incoming state C h^T), and across chunks as a
+ * recurrence over the chunk states. fp32 arithmetic throughout (bf16 inputs are widened).
+ *
+ * Layouts (row-major, contiguous):
+ *   x, y    : (batch, seqlen, n_heads, head_dim), activation dtype
+ *   dt_raw  : (batch, seqlen, n_heads), activation dtype
+ *   B, C    : (batch, seqlen, d_state), activation dtype
+ *   A_log, D, dt_bias : (n_heads) fp32
+ *   state   : (batch, n_heads, head_dim, d_state) fp32
+ * Supported: head_dim == 64 and d_state == 128 (else AXON_ERR_UNSUPPORTED); batch and n_heads in
+ * [1, 65535] (0 or negative: AXON_ERR_INVALID_ARGUMENT; larger: AXON_ERR_UNSUPPORTED);
+ * seqlen >= 0; batch*seqlen*n_heads*head_dim <= 2^40. Pointers are device memory owned by the
+ * caller, 16-byte aligned; errors as for axon_ssm_prefill. */
+typedef struct {
+  int64_t batch;     /* B */
+  int64_t seqlen;    /* L */
+  int64_t n_heads;   /* H */
+  int64_t head_dim;  /* P, must be 64 */
+  int64_t d_state;   /* N, must be 128 */
+  axon_dtype act_dtype;
+} axon_ssd_shape;
+
+typedef struct {
+  const float* A_log;    /* (H) */
+  const float* D;        /* (H) */
+  const float* dt_bias;  /* (H) */
+  float dt_min;
+  float dt_max;
+} axon_ssd_params;
+
+/* Bytes of device workspace axon_ssd_scan needs (0 for an invalid shape or seqlen == 0). */
+size_t axon_ssd_scan_workspace_bytes(const axon_ssd_shape* shape);
+
+/* Runs the SSD core over seqlen tokens. state_in (B, H, P, N) may be NULL (zeros); state_out
+ * receives the state after the last token and may equal state_in (in place) but must not
+ * partially overlap it. y must not overlap any input. seqlen == 0 copies state_in to state_out
+ * (zeros for NULL) and writes no y. Running L1 tokens then L2 from the returned state equals
+ * running L1 + L2 up to rounding. workspace: axon_ssd_scan_workspace_bytes(shape) bytes,
+ * 16-byte aligned, no initialisation needed. */
+axon_status axon_ssd_scan(const axon_ssd_shape* shape, const axon_ssd_params* params,
+                          const void* x, const void* dt_raw, const void* B, const void* C,
+                          const float* state_in, void* y, float* state_out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -55,6 +55,17 @@ class LayerWeights(ctypes.Structure):
                 ("ssm", Params)]
 
 
+class SsdShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("n_heads", ctypes.c_int64),
+                ("head_dim", ctypes.c_int64), ("d_state", ctypes.c_int64),
+                ("act_dtype", ctypes.c_int)]
+
+
+class SsdParams(ctypes.Structure):
+    _fields_ = [("A_log", ctypes.c_void_p), ("D", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float)]
+
+
 CONV_ACTIVATIONS = {"none": 0, "silu": 1}
 DISCRETIZATIONS = {"first_order": 0, "zoh": 1}
 
@@ -98,6 +109,11 @@ def load():
         lib.axon_layer_forward.argtypes = [
             P, ctypes.POINTER(LayerShape), ctypes.POINTER(LayerWeights), P, P, P, P, P, P, P,
             ctypes.c_size_t, P]
+        lib.axon_ssd_scan_workspace_bytes.restype = ctypes.c_size_t
+        lib.axon_ssd_scan_workspace_bytes.argtypes = [ctypes.POINTER(SsdShape)]
+        lib.axon_ssd_scan.restype = ctypes.c_int
+        lib.axon_ssd_scan.argtypes = [ctypes.POINTER(SsdShape), ctypes.POINTER(SsdParams),
+                                      P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         _lib = lib
         return lib
 
@@ -172,6 +188,22 @@ def raw_layer_forward(ctx, shape: LayerShape, weights: LayerWeights, x_in, cache
     return load().axon_layer_forward(ctx, ctypes.byref(shape), ctypes.byref(weights), x_in,
                                      cache_in, state_in, out, cache_out, state_out, workspace,
                                      int(workspace_bytes_), stream)
+
+
+def make_ssd_shape(batch, seqlen, n_heads, act_bf16, head_dim=64, d_state=128) -> SsdShape:
+    return SsdShape(int(batch), int(seqlen), int(n_heads), int(head_dim), int(d_state),
+                    AXON_BF16 if act_bf16 else AXON_F32)
+
+
+def ssd_workspace_bytes(shape: SsdShape) -> int:
+    return int(load().axon_ssd_scan_workspace_bytes(ctypes.byref(shape)))
+
+
+def raw_ssd_scan(shape: SsdShape, params: SsdParams, x, dt_raw, B, C, state_in, y, state_out,
+                 workspace, workspace_bytes_, stream) -> int:
+    """axon_ssd_scan with integer pointers. Returns the status code."""
+    return load().axon_ssd_scan(ctypes.byref(shape), ctypes.byref(params), x, dt_raw, B, C,
+                                state_in, y, state_out, workspace, int(workspace_bytes_), stream)
 
 
 def declared_functions() -> list[str]:

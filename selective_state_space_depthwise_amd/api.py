@@ -216,3 +216,57 @@ class Layer:
         if st != _abi.AXON_OK:
             raise AxonError(st, "axon_layer_forward")
         return out, conv_cache_out, ssm_state_out
+
+
+SSD_HEAD_DIM = 64
+SSD_STATE = 128
+
+
+def ssd_workspace_bytes(batch: int, seqlen: int, n_heads: int, bf16: bool = False) -> int:
+    """Device workspace bytes axon_ssd_scan needs for this shape."""
+    return _abi.ssd_workspace_bytes(_abi.make_ssd_shape(batch, seqlen, n_heads, bf16))
+
+
+def ssd_scan(x, dt_raw, B, C, A_log, D, dt_bias, *, dt_min=1e-4, dt_max=100.0, state_in=None,
+             y=None, state_out=None, workspace=None, stream=None):
+    """Mamba-2 SSD core on the GPU: x (B, L, H, 64), dt_raw (B, L, H), B, C (B, L, 128), float32
+    or bfloat16 (all the same dtype); A_log, D, dt_bias (H,) float32; optional state_in
+    (B, H, 64, 128) float32 (None = zeros). Returns (y, state_out); state_out may be state_in
+    (in place). Asynchronous on ``stream`` (default: torch's current stream)."""
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError("ssd_scan runs on the GPU only; x is on " + str(device))
+    bf16 = _act_dtype(x)
+    if x.dim() != 4:
+        raise ValueError("x must be (batch, seqlen, n_heads, head_dim)")
+    Bsz, L, H, P = x.shape
+    _check(x, "x", (Bsz, L, H, SSD_HEAD_DIM), x.dtype, device)
+    _check(dt_raw, "dt_raw", (Bsz, L, H), x.dtype, device)
+    for t, n in ((B, "B"), (C, "C")):
+        _check(t, n, (Bsz, L, SSD_STATE), x.dtype, device)
+    for t, n in ((A_log, "A_log"), (D, "D"), (dt_bias, "dt_bias")):
+        _check(t, n, (H,), torch.float32, device)
+    state_shape = (Bsz, H, SSD_HEAD_DIM, SSD_STATE)
+    if state_in is not None:
+        _check(state_in, "state_in", state_shape, torch.float32, device)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", tuple(x.shape), x.dtype, device)
+    if state_out is None:
+        state_out = torch.empty(state_shape, dtype=torch.float32, device=device)
+    _check(state_out, "state_out", state_shape, torch.float32, device)
+    shape = _abi.make_ssd_shape(Bsz, L, H, bf16)
+    prm = _abi.SsdParams(A_log.data_ptr(), D.data_ptr(), dt_bias.data_ptr(), float(dt_min),
+                         float(dt_max))
+    need = _abi.ssd_workspace_bytes(shape)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _abi.raw_ssd_scan(shape, prm, x.data_ptr(), dt_raw.data_ptr(), B.data_ptr(),
+                           C.data_ptr(), state_in.data_ptr() if state_in is not None else None,
+                           y.data_ptr(), state_out.data_ptr(), ws_ptr, ws_bytes,
+                           _stream_handle(device, stream))
+    if st != _abi.AXON_OK:
+        raise AxonError(st, "axon_ssd_scan")
+    return y, state_out

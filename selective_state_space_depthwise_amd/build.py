@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libaxonscan.so")
 
-HIP_SOURCES = ["axon_kernels.hip", "axon_rowscan.hip", "axon_layer.hip"]
+HIP_SOURCES = ["axon_kernels.hip", "axon_rowscan.hip", "axon_layer.hip", "axon_ssd.hip"]
 CXX_SOURCES = ["axonscan_api.cpp"]
 ARCH = "gfx950"
 ROCM_LIB = "/opt/rocm/lib"  # hipBLASLt (the layer's projection GEMMs)

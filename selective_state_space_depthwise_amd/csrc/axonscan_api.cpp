@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0: variant fields in axon_ssm_params
+constexpr int kVersion = 300;  // 0.3.0: the Mamba-2 SSD core (axon_ssd_scan)
 constexpr int64_t kMaxBatch = 65535;      // launch grid y dimension
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 // The prefill kernels address a tile of (32 + 3) tokens x d_inner channels with byte offsets

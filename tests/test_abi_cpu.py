@@ -53,7 +53,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert A.version() == 200
+    assert A.version() == 300
     for st in range(5):
         assert A.status_string(st)
     assert A.status_string(99) == "unknown status"
@@ -225,3 +225,68 @@ def test_layer_forward_rejects_bad_arguments():
                         conv_activation=3)
     assert _lforward(params=bad) == A.AXON_ERR_UNSUPPORTED
     assert _lforward() == A.AXON_ERR_INVALID_ARGUMENT                 # context without a handle
+
+
+# ---- Mamba-2 SSD core ----------------------------------------------------------------------------
+def _ssd_shape(batch=1, seqlen=200, heads=4, bf16=False, head_dim=64, d_state=128):
+    return A.make_ssd_shape(batch, seqlen, heads, bf16, head_dim=head_dim, d_state=d_state)
+
+
+def _ssd_params(dt_min=1e-4, dt_max=100.0, base=P + (1 << 30)):
+    return A.SsdParams(base, base + (1 << 20), base + (2 << 20), dt_min, dt_max)
+
+
+def _ssd(shape=None, params=None, ws_bytes=1 << 30, **over):
+    b = _buffers()
+    b.update(over)
+    return A.raw_ssd_scan(shape or _ssd_shape(), params or _ssd_params(), b["x"], b["dt"],
+                          b["B"], b["C"], b["sin"], b["y"], b["sout"], b["ws"], ws_bytes, None)
+
+
+def test_ssd_workspace_is_a_pure_function_of_shape():
+    # (B, H, chunks, 64, 128) chunk states + (B, H, chunks) decays + (B, chunks, 64, 64) C B^T,
+    # each rounded up to 256 bytes
+    n = A.ssd_workspace_bytes(_ssd_shape(batch=1, seqlen=2048, heads=64))
+    assert n == 64 * 32 * 64 * 128 * 4 + 64 * 32 * 4 + 32 * 64 * 64 * 4
+    assert A.ssd_workspace_bytes(_ssd_shape(seqlen=65, heads=1)) == (2 * 8192 * 4 + 256 +
+                                                                     2 * 4096 * 4)
+    assert A.ssd_workspace_bytes(_ssd_shape(seqlen=0)) == 0
+    assert A.ssd_workspace_bytes(_ssd_shape(head_dim=32)) == 0
+    assert A.ssd_workspace_bytes(_ssd_shape(batch=0)) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=32), A.AXON_ERR_UNSUPPORTED), (dict(d_state=64), A.AXON_ERR_UNSUPPORTED),
+    (dict(batch=65536), A.AXON_ERR_UNSUPPORTED), (dict(heads=65536), A.AXON_ERR_UNSUPPORTED),
+    (dict(batch=0), A.AXON_ERR_INVALID_ARGUMENT), (dict(heads=0), A.AXON_ERR_INVALID_ARGUMENT),
+    (dict(seqlen=-1), A.AXON_ERR_INVALID_ARGUMENT),
+    (dict(batch=1 << 20, seqlen=1 << 20, heads=1 << 10), A.AXON_ERR_UNSUPPORTED),
+    (dict(batch=60000, seqlen=1 << 20, heads=60000), A.AXON_ERR_INVALID_ARGUMENT),
+])
+def test_ssd_rejects_bad_shapes(kw, status):
+    assert _ssd(_ssd_shape(**kw)) == status
+
+
+def test_ssd_rejects_bad_arguments():
+    assert A.load().axon_ssd_scan(None, ctypes.byref(_ssd_params()), P, P, P, P, None, P, P, P,
+                                  1 << 30, None) == A.AXON_ERR_INVALID_ARGUMENT
+    assert A.load().axon_ssd_scan(ctypes.byref(_ssd_shape()), None, P, P, P, P, None, P, P, P,
+                                  1 << 30, None) == A.AXON_ERR_INVALID_ARGUMENT
+    bad = A.make_ssd_shape(1, 64, 2, False)
+    bad.act_dtype = 7
+    assert _ssd(bad) == A.AXON_ERR_UNSUPPORTED
+    for name in ("x", "dt", "B", "C", "y", "sout"):
+        assert _ssd(**{name: 0}) == A.AXON_ERR_INVALID_ARGUMENT, name
+        assert _ssd(**{name: _buffers()[name] + 4}) == A.AXON_ERR_INVALID_ARGUMENT, name
+    assert _ssd(sin=_buffers()["sin"] + 8) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _ssd(params=_ssd_params(dt_min=-1.0)) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _ssd(params=_ssd_params(dt_min=2.0, dt_max=1.0)) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _ssd(params=_ssd_params(dt_max=float("inf"))) == A.AXON_ERR_INVALID_ARGUMENT
+    need = A.ssd_workspace_bytes(_ssd_shape())
+    assert _ssd(ws_bytes=need - 1) == A.AXON_ERR_WORKSPACE_TOO_SMALL
+    assert _ssd(ws=0, ws_bytes=need) == A.AXON_ERR_INVALID_ARGUMENT
+    b = _buffers()
+    assert _ssd(y=b["x"] + 256) == A.AXON_ERR_INVALID_ARGUMENT       # y overlaps x
+    assert _ssd(ws=b["B"]) == A.AXON_ERR_INVALID_ARGUMENT             # workspace overlaps B
+    assert _ssd(sout=b["sin"] + 1024) == A.AXON_ERR_INVALID_ARGUMENT  # partial state overlap
+    assert _ssd(sout=b["y"]) == A.AXON_ERR_INVALID_ARGUMENT          # state out overlaps y

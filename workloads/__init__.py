@@ -197,3 +197,72 @@ def workload(name_or_index) -> Workload:
         if w.name == name_or_index:
             return w
     raise KeyError(name_or_index)
+
+
+# ---- Mamba-2 SSD core ----------------------------------------------------------------------------
+# Block shape of "Selective State Space Models (Mamba)", pattern "Mamba-2 block": d_model 2048,
+# expand 2 (d_inner 4096), headdim 64 -> 64 heads, d_state 128. The pages give no sequence
+# length for it; the Axon-SSM headline length (2048, batch 1) is used.
+SSD_HEAD_DIM = 64
+SSD_STATE = 128
+SSD_SEED_BASE = 0x55D000
+TID_SSD_X, TID_SSD_DT, TID_SSD_B, TID_SSD_C, TID_SSD_ALOG, TID_SSD_D, TID_SSD_DTB = range(31, 38)
+
+
+@dataclass(frozen=True)
+class SsdWorkload:
+    index: int
+    name: str
+    batch: int
+    seqlen: int
+    heads: int
+    act: str
+    dt_mode: str = "axon"
+
+    @property
+    def seed(self) -> int:
+        return SSD_SEED_BASE + self.index
+
+
+SSD_WORKLOADS = [
+    SsdWorkload(0, "mamba2_ssd_f32_b1_l2048_h64", 1, 2048, 64, "f32"),
+    SsdWorkload(1, "mamba2_ssd_bf16_b1_l2048_h64", 1, 2048, 64, "bf16"),
+]
+
+
+def ssd_inputs(w: SsdWorkload, batch: int | None = None, seqlen: int | None = None,
+               heads: int | None = None, seed_offset: int = 0) -> dict:
+    """Inputs of the SSD core: x (B, L, H, 64), dt_raw (B, L, H), B, C (B, L, 128) ~ N(0, 1);
+    per head A_log = log(U[1, 16]) (A in [-16, -1]), D ~ N(0, 1), dt_bias = log(expm1(U)) with
+    U ~ U[1e-3, 0.1] (or log-uniform on [1e-4, 1] plus about 1% of dt_raw at +-50 for
+    dt_mode "wide"), dt clipped to [1e-4, 100]. bf16 workloads round the activations."""
+    Bsz = batch or w.batch
+    L = w.seqlen if seqlen is None else seqlen
+    H = heads or w.heads
+    seed = w.seed + 7919 * seed_offset
+    out = {
+        "x": _normal(seed, TID_SSD_X, (Bsz, L, H, SSD_HEAD_DIM)),
+        "dt_raw": _normal(seed, TID_SSD_DT, (Bsz, L, H)),
+        "B": _normal(seed, TID_SSD_B, (Bsz, L, SSD_STATE)),
+        "C": _normal(seed, TID_SSD_C, (Bsz, L, SSD_STATE)),
+    }
+    if w.dt_mode == "wide":
+        hit = _rng(seed, TID_MASK).random(size=(Bsz, L, H), dtype=np.float32) < 0.01
+        sign = _rng(seed, TID_SIGN).random(size=(Bsz, L, H), dtype=np.float32) < 0.5
+        out["dt_raw"] = np.where(hit, np.where(sign, np.float32(50.0), np.float32(-50.0)),
+                                 out["dt_raw"]).astype(np.float32)
+    if w.act == "bf16":
+        for k in ("x", "dt_raw", "B", "C"):
+            out[k] = bf16_round(out[k])
+    g = _rng(w.seed, TID_SSD_DTB)
+    if w.dt_mode == "wide":
+        U = np.exp(g.uniform(np.log(1e-4), np.log(1.0), size=H))
+    else:
+        U = g.uniform(1e-3, 0.1, size=H)
+    out["dt_bias"] = np.log(np.expm1(U)).astype(np.float32)
+    out["A_log"] = np.log(_rng(w.seed, TID_SSD_ALOG).uniform(1.0, 16.0, size=H)).astype(
+        np.float32)
+    out["D"] = _normal(w.seed, TID_SSD_D, (H,))
+    out["dt_min"], out["dt_max"] = DT_MIN, DT_MAX
+    out["act"] = w.act
+    return out
