@@ -108,9 +108,12 @@ __device__ __forceinline__ float exp2_diff(float hi_a, float lo_a, float hi_b, f
   return __builtin_amdgcn_exp2f((hi_a - hi_b) + (lo_a - lo_b));
 }
 
+// Contraction over the 128 states in the gram and output kernels: k-step (jb, jj), jb = 0..7,
+// jj = 0..3, lane group g takes n = 16 jb + 4 g + jj, so one 16-byte load per lane and jb gives
+// a 16-lane row block 64 contiguous bytes per row.
+
 // ---- G_c = C_c B_c^T -----------------------------------------------------------------------
 // Grid (nc, B), 4 waves; wave w computes the 16-row block w against column blocks 0..w.
-// Contraction index n = 32 g + j at k-step j, so each lane reads 32 consecutive states.
 template <typename Act>
 __global__ __launch_bounds__(kThreads) void ssd_gram_kernel(SsdArgs a) {
   const int c = blockIdx.x;
@@ -119,28 +122,29 @@ __global__ __launch_bounds__(kThreads) void ssd_gram_kernel(SsdArgs a) {
   const int64_t tok0 = int64_t(c) * kQ;
   const Act* Cp = static_cast<const Act*>(a.C);
   const Act* Bp = static_cast<const Act*>(a.B);
-  float crow[32];
+  float4 crow[8];
   {
     const int64_t tok = tok0 + 16 * w + i;
     const bool ok = tok < a.seqlen;
 #pragma unroll
-    for (int j = 0; j < 32; j += 4) {
-      const float4 v = ok ? load4(Cp, (b * a.seqlen + tok) * kN + 32 * g + j) : float4{};
-      crow[j] = v.x, crow[j + 1] = v.y, crow[j + 2] = v.z, crow[j + 3] = v.w;
-    }
+    for (int jb = 0; jb < 8; ++jb)
+      crow[jb] = ok ? load4(Cp, (b * a.seqlen + tok) * kN + 16 * jb + 4 * g) : float4{};
   }
   float* G = a.gram + (b * a.nchunks + c) * int64_t(kQ * kQ);
   for (int st = 0; st <= w; ++st) {
     const int64_t tok = tok0 + 16 * st + i;
     const bool ok = tok < a.seqlen;
+    float4 brow[8];
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb)
+      brow[jb] = ok ? load4(Bp, (b * a.seqlen + tok) * kN + 16 * jb + 4 * g) : float4{};
     f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < 32; j += 4) {
-      const float4 v = ok ? load4(Bp, (b * a.seqlen + tok) * kN + 32 * g + j) : float4{};
-      acc = mfma4(crow[j], v.x, acc);
-      acc = mfma4(crow[j + 1], v.y, acc);
-      acc = mfma4(crow[j + 2], v.z, acc);
-      acc = mfma4(crow[j + 3], v.w, acc);
+    for (int jb = 0; jb < 8; ++jb) {
+      acc = mfma4(crow[jb].x, brow[jb].x, acc);
+      acc = mfma4(crow[jb].y, brow[jb].y, acc);
+      acc = mfma4(crow[jb].z, brow[jb].z, acc);
+      acc = mfma4(crow[jb].w, brow[jb].w, acc);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) G[(16 * w + 4 * g + r) * kQ + 16 * st + i] = acc[r];
@@ -149,8 +153,10 @@ __global__ __launch_bounds__(kThreads) void ssd_gram_kernel(SsdArgs a) {
 
 // ---- S_c = x^T diag(w) B --------------------------------------------------------------------
 // Grid (nc, H, B), 4 waves. The chunk's x (scaled by w_s = exp(cum_last - cum_s) dt_s) and B
-// are staged in LDS; wave w computes rows p = 16 w .. 16 w + 15 of S against all 8 column
-// blocks, contraction index s = 4 j + g. Row strides of 80 and 144 floats put the four lane
+// are staged in LDS. Wave w computes S^T for the head channels p = 16 w .. 16 w + 15 against
+// all 8 blocks of 16 states, A operand B^T (rows n), B operand the scaled x (columns p),
+// contraction index s = 4 j + g; the result D[n][p] leaves every lane 4 consecutive states of
+// one channel, stored as one 16-byte write. Row strides of 80 and 144 floats put the four lane
 // groups of one LDS read in disjoint banks.
 constexpr int kXS = kP + 16;
 constexpr int kBS = kN + 16;
@@ -207,38 +213,47 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(SsdArgs a) {
 #pragma unroll 4
   for (int j = 0; j < 16; ++j) {
     const int s = 4 * j + g;
-    const float av = xs[s * kXS + 16 * w + i];
+    const float xv = xs[s * kXS + 16 * w + i];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) acc[nt] = mfma4(av, bs[s * kBS + 16 * nt + i], acc[nt]);
+    for (int nt = 0; nt < 8; ++nt) acc[nt] = mfma4(bs[s * kBS + 16 * nt + i], xv, acc[nt]);
   }
-  float* S = a.states + (bh * a.nchunks + c) * int64_t(kP * kN);
+  float* S = a.states + (bh * a.nchunks + c) * int64_t(kP * kN) + (16 * w + i) * kN + 4 * g;
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) S[(16 * w + 4 * g + r) * kN + 16 * nt + i] = acc[nt][r];
+    *reinterpret_cast<float4*>(S + 16 * nt) =
+        make_float4(acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]);
 }
 
 // ---- recurrence over chunks -----------------------------------------------------------------
 // Grid (P N / 4 / 256, H, B): one float4 of the (P, N) state per thread. In place: slot c of
-// the states buffer holds S_c on entry and H_c (the state entering chunk c) on exit.
+// the states buffer holds S_c on entry and H_c (the state entering chunk c) on exit. The loads
+// of 8 chunks are issued together, so one memory latency covers 8 steps of the recurrence.
 __global__ __launch_bounds__(kThreads) void ssd_pass_kernel(SsdArgs a) {
   constexpr int kVec = kP * kN / 4;
+  constexpr int kDepth = 8;
   const int i4 = blockIdx.x * kThreads + threadIdx.x;
   const int64_t bh = int64_t(blockIdx.z) * a.heads + blockIdx.y;
   float4 hs = a.state_in ? reinterpret_cast<const float4*>(a.state_in)[bh * kVec + i4]
                          : float4{0.0f, 0.0f, 0.0f, 0.0f};
   float4* S = reinterpret_cast<float4*>(a.states + bh * a.nchunks * int64_t(kP * kN)) + i4;
   const float* dec = a.decay + bh * a.nchunks;
-  float4 nxt = S[0];
-  for (int c = 0; c < a.nchunks; ++c) {
-    const float4 cur = nxt;
-    if (c + 1 < a.nchunks) nxt = S[int64_t(c + 1) * kVec];
-    S[int64_t(c) * kVec] = hs;
-    const float d = dec[c];
-    hs.x = fmaf(d, hs.x, cur.x);
-    hs.y = fmaf(d, hs.y, cur.y);
-    hs.z = fmaf(d, hs.z, cur.z);
-    hs.w = fmaf(d, hs.w, cur.w);
+  for (int c0 = 0; c0 < a.nchunks; c0 += kDepth) {
+    const int n = a.nchunks - c0 < kDepth ? a.nchunks - c0 : kDepth;
+    float4 v[kDepth];
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k)
+      if (k < n) v[k] = S[int64_t(c0 + k) * kVec];
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      if (k < n) {
+        S[int64_t(c0 + k) * kVec] = hs;
+        const float d = dec[c0 + k];
+        hs.x = fmaf(d, hs.x, v[k].x);
+        hs.y = fmaf(d, hs.y, v[k].y);
+        hs.z = fmaf(d, hs.z, v[k].z);
+        hs.w = fmaf(d, hs.w, v[k].w);
+      }
+    }
   }
   reinterpret_cast<float4*>(a.state_out)[bh * kVec + i4] = hs;
 }
@@ -254,16 +269,20 @@ __global__ __launch_bounds__(kThreads) void ssd_copy_state_kernel(const float* i
 
 // ---- outputs ---------------------------------------------------------------------------------
 // Grid (nc, H, B), 4 waves; wave w owns tokens 16 w .. 16 w + 15 of the chunk and all 64 head
-// channels (4 column blocks). Incoming-state term: contraction over n = 32 g + j with C rows and
-// H_c rows read straight from global memory (H_c is shared by the 4 waves through the caches);
-// then each row is scaled by exp2(cum_t). Intra-chunk term: contraction over s = 16 st + 4 g + j
-// for the column blocks st <= w, the A operand being G scaled by the decay mask, the B operand
-// x from LDS (row stride 68 floats: the four lane groups, 4 rows apart, hit disjoint banks).
+// channels (4 column blocks). H_c (64 x 128) is staged in LDS once per workgroup (row stride
+// 132 floats: the 16 rows of one 16-byte LDS read fall in distinct banks); the C rows of the
+// wave's tokens come straight from global memory. Incoming-state term: contraction over the
+// states, then each row scaled by exp2(cum_t). Intra-chunk term: contraction over
+// s = 16 st + 4 g + j for the column blocks st <= w, the A operand being G scaled by the decay
+// mask, the B operand x from LDS (row stride 68 floats: the four lane groups, 4 rows apart,
+// hit disjoint banks).
 constexpr int kXO = kP + 4;
+constexpr int kHO = kN + 4;
 
 template <typename Act>
 __global__ __launch_bounds__(kThreads) void ssd_output_kernel(SsdArgs a) {
   __shared__ float xs[kQ * kXO];
+  __shared__ float hsm[kP * kHO];
   __shared__ float cum_hi[kQ];
   __shared__ float cum_lo[kQ];
   __shared__ float dts[kQ];
@@ -290,31 +309,38 @@ __global__ __launch_bounds__(kThreads) void ssd_output_kernel(SsdArgs a) {
                           : float4{};
       *reinterpret_cast<float4*>(&xs[t * kXO + 16 * q + j]) = v;
     }
+    // H_c: thread -> channel tid / 4, states 32 (tid % 4) .. + 31
+    const float* Hc = a.states + (bh * a.nchunks + c) * int64_t(kP * kN) + t * kN + 32 * q;
+#pragma unroll
+    for (int j = 0; j < 32; j += 4)
+      *reinterpret_cast<float4*>(&hsm[t * kHO + 32 * q + j]) =
+          *reinterpret_cast<const float4*>(Hc + j);
   }
-  // Incoming-state term (needs neither LDS array).
+  float4 crow[8];
+  {
+    const int64_t tok = tok0 + 16 * w + i;
+    const bool ok = tok < a.seqlen;
+    const Act* Cp = static_cast<const Act*>(a.C);
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb)
+      crow[jb] = ok ? load4(Cp, (b * a.seqlen + tok) * kN + 16 * jb + 4 * g) : float4{};
+  }
+  __syncthreads();  // xs, hsm, cum_hi, cum_lo, dts ready
   f4 acc[4];
 #pragma unroll
   for (int pt = 0; pt < 4; ++pt) acc[pt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-  {
-    const int t = 16 * w + i;
-    const int64_t tok = tok0 + t;
-    const bool ok = tok < a.seqlen;
-    const Act* Cp = static_cast<const Act*>(a.C);
-    const float* Hc = a.states + (bh * a.nchunks + c) * int64_t(kP * kN);
 #pragma unroll
-    for (int j = 0; j < 32; j += 4) {
-      const float4 cv = ok ? load4(Cp, (b * a.seqlen + tok) * kN + 32 * g + j) : float4{};
+  for (int jb = 0; jb < 8; ++jb) {
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const float4 hv = *reinterpret_cast<const float4*>(Hc + (16 * pt + i) * kN + 32 * g + j);
-        acc[pt] = mfma4(cv.x, hv.x, acc[pt]);
-        acc[pt] = mfma4(cv.y, hv.y, acc[pt]);
-        acc[pt] = mfma4(cv.z, hv.z, acc[pt]);
-        acc[pt] = mfma4(cv.w, hv.w, acc[pt]);
-      }
+    for (int pt = 0; pt < 4; ++pt) {
+      const float4 hv = *reinterpret_cast<const float4*>(&hsm[(16 * pt + i) * kHO + 16 * jb +
+                                                               4 * g]);
+      acc[pt] = mfma4(crow[jb].x, hv.x, acc[pt]);
+      acc[pt] = mfma4(crow[jb].y, hv.y, acc[pt]);
+      acc[pt] = mfma4(crow[jb].z, hv.z, acc[pt]);
+      acc[pt] = mfma4(crow[jb].w, hv.w, acc[pt]);
     }
   }
-  __syncthreads();  // xs, cum_hi, cum_lo, dts ready
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = 16 * w + 4 * g + r;
