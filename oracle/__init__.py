@@ -274,16 +274,18 @@ def layer_forward(x_in, W_in, W_f, W_out, params: dict, conv_cache_in=None, ssm_
 
 
 # ---- Mamba-2 SSD core ----------------------------------------------------------------------------
-def ssd_scan(inp: dict, state_in=None, threads: int = 1, lib=None) -> dict:
+def ssd_scan(inp: dict, state_in=None, threads: int = 1, lib=None,
+             magnitude: bool = False) -> dict:
     """The SSD core over x (B, L, H, P), dt_raw (B, L, H), B, C (B, L, N) float32 with A_log,
     D, dt_bias (H,) and the dt clips (see oracle_ssd_scan). Returns y (B, L, H, P) and
-    ssm_state (B, H, P, N), float64."""
+    ssm_state (B, H, P, N), float64, and with ``magnitude`` also ``mag`` (B, L, H, P):
+    sum_n |C h| + |D x|, the size of the terms each output sums."""
     lib = _load(lib)
     if not hasattr(lib, "_ssd_declared"):
         P_, I_, D_ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double
         lib.oracle_ssd_scan.restype = ctypes.c_int
         lib.oracle_ssd_scan.argtypes = [I_, I_, I_, I_, I_, P_, P_, P_, P_, P_, P_, P_, D_, D_,
-                                        P_, P_, P_, ctypes.c_int]
+                                        P_, P_, P_, P_, ctypes.c_int]
         lib._ssd_declared = True
     x, dtr = _f32(inp["x"]), _f32(inp["dt_raw"])
     Bm, Cm = _f32(inp["B"]), _f32(inp["C"])
@@ -295,10 +297,15 @@ def ssd_scan(inp: dict, state_in=None, threads: int = 1, lib=None) -> dict:
         assert sin.shape == (Bsz, H, P, N)
     y = np.empty((Bsz, L, H, P), np.float64)
     sout = np.empty((Bsz, H, P, N), np.float64)
+    mag = np.empty((Bsz, L, H, P), np.float64) if magnitude else None
     rc = lib.oracle_ssd_scan(Bsz, L, H, P, N, _ptr(x), _ptr(dtr), _ptr(Bm), _ptr(Cm),
                              _ptr(_f32(inp["A_log"])), _ptr(_f32(inp["D"])),
                              _ptr(_f32(inp["dt_bias"])), float(inp["dt_min"]),
-                             float(inp["dt_max"]), _ptr(sin), _ptr(y), _ptr(sout), int(threads))
+                             float(inp["dt_max"]), _ptr(sin), _ptr(y), _ptr(sout), _ptr(mag),
+                             int(threads))
     if rc != 0:
         raise ValueError("oracle_ssd_scan rejected its arguments")
-    return {"y": y, "ssm_state": sout}
+    out = {"y": y, "ssm_state": sout}
+    if magnitude:
+        out["mag"] = mag
+    return out

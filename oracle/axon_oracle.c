@@ -236,7 +236,7 @@ typedef struct {
   const float *x, *dt_raw, *Bm, *Cm, *A_log, *D, *dt_bias;
   double dt_min, dt_max;
   const double* state_in;
-  double *y, *state_out;
+  double *y, *state_out, *mag;
   int64_t begin, end; /* (b, head) index range */
   int status;
 } ssd_job;
@@ -260,13 +260,16 @@ static void* ssd_worker(void* arg) {
       const float* Bt = j->Bm + (b * L + t) * N;
       const float* Ct = j->Cm + (b * L + t) * N;
       double* yt = j->y + ((b * L + t) * H + hd) * P;
+      double* mt = j->mag ? j->mag + ((b * L + t) * H + hd) * P : NULL;
       for (int64_t p = 0; p < P; ++p) {
-        double acc = 0.0;
+        double acc = 0.0, size = 0.0;
         for (int64_t n = 0; n < N; ++n) {
           h[p * N + n] = a * h[p * N + n] + dt * (double)xt[p] * (double)Bt[n];
           acc += (double)Ct[n] * h[p * N + n];
+          size += fabs((double)Ct[n] * h[p * N + n]);
         }
         yt[p] = acc + (double)j->D[hd] * (double)xt[p];
+        if (mt) mt[p] = size + fabs((double)j->D[hd] * (double)xt[p]);
       }
     }
     for (int64_t i = 0; i < P * N; ++i) j->state_out[bh * P * N + i] = h[i];
@@ -279,7 +282,7 @@ int oracle_ssd_scan(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N,
                     const float* x, const float* dt_raw, const float* Bm, const float* Cm,
                     const float* A_log, const float* D, const float* dt_bias, double dt_min,
                     double dt_max, const double* state_in, double* y, double* state_out,
-                    int threads) {
+                    double* mag, int threads) {
   if (Bsz < 1 || L < 0 || H < 1 || P < 1 || N < 1 || !A_log || !D || !dt_bias || !state_out)
     return -1;
   if (L > 0 && (!x || !dt_raw || !Bm || !Cm || !y)) return -1;
@@ -292,7 +295,8 @@ int oracle_ssd_scan(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N,
   int started[256];
   for (int i = 0; i < threads; ++i) {
     ssd_job jb = {Bsz, L, H, P, N, x, dt_raw, Bm, Cm, A_log, D, dt_bias, dt_min, dt_max,
-                  state_in, y, state_out, total * i / threads, total * (i + 1) / threads, 0};
+                  state_in, y, state_out, mag, total * i / threads, total * (i + 1) / threads,
+                  0};
     jobs[i] = jb;
     started[i] = 0;
   }

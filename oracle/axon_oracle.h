@@ -93,12 +93,14 @@ extern "C" {
  *   h_t[p, n] = exp(dt_t A) h_{t-1}[p, n] + dt_t x_t[p] B_t[n]
  *   y_t[p]    = sum_n C_t[n] h_t[p, n] + D x_t[p]
  * x, y (B, L, H, P); dt_raw (B, L, H); Bm, Cm (B, L, N) shared by all heads; A_log, D, dt_bias
- * (H); state_in / state_out (B, H, P, N) (state_in NULL = zeros). Returns 0 or -1. */
+ * (H); state_in / state_out (B, H, P, N) (state_in NULL = zeros); mag (B, L, H, P) or NULL:
+ * sum_n |C_t[n] h_t[p, n]| + |D x_t[p]|, the size of the terms y sums (for tolerances of
+ * ill-conditioned outputs). Returns 0 or -1. */
 int oracle_ssd_scan(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N,
                     const float* x, const float* dt_raw, const float* Bm, const float* Cm,
                     const float* A_log, const float* D, const float* dt_bias, double dt_min,
                     double dt_max, const double* state_in, double* y, double* state_out,
-                    int threads);
+                    double* mag, int threads);
 
 #ifdef __cplusplus
 }

@@ -248,6 +248,8 @@ def test_ssd_workspace_is_a_pure_function_of_shape():
     # each rounded up to 256 bytes
     n = A.ssd_workspace_bytes(_ssd_shape(batch=1, seqlen=2048, heads=64))
     assert n == 64 * 32 * 64 * 128 * 4 + 64 * 32 * 4 + 32 * 64 * 64 * 4
+    n = A.ssd_workspace_bytes(_ssd_shape(batch=1, seqlen=2048, heads=63))
+    assert n == 63 * 32 * 64 * 128 * 4 + 8192 + 32 * 64 * 64 * 4  # 63 * 32 * 4 rounds up
     assert A.ssd_workspace_bytes(_ssd_shape(seqlen=65, heads=1)) == (2 * 8192 * 4 + 256 +
                                                                      2 * 4096 * 4)
     assert A.ssd_workspace_bytes(_ssd_shape(seqlen=0)) == 0
