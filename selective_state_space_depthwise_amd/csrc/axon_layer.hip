@@ -35,31 +35,107 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 // u[b, t, e] = conv_b[e] + sum_k w[e, k] x~[b, t - 3 + k, e], x~ = [cache_in, x] (zeros without a
 // cache), then SiLU for the Mamba-block variant; the same accumulation order as the prefill
 // kernel's prologue.
-template <typename Act, bool kSilu>
+// Vector of V consecutive activations (V = 4: one 16-byte fp32 or 8-byte bf16 access).
+template <int V>
+__device__ __forceinline__ void load_vec(const float* p, int64_t i, float (&v)[V]) {
+  if constexpr (V == 4) {
+    const float4 q = *reinterpret_cast<const float4*>(p + i);
+    v[0] = q.x, v[1] = q.y, v[2] = q.z, v[3] = q.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < V; ++k) v[k] = p[i + k];
+  }
+}
+template <int V>
+__device__ __forceinline__ void load_vec(const bf16_bits* p, int64_t i, float (&v)[V]) {
+  if constexpr (V == 4) {
+    const uint2 q = *reinterpret_cast<const uint2*>(p + i);
+    v[0] = __uint_as_float(q.x << 16), v[1] = __uint_as_float(q.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(q.y << 16), v[3] = __uint_as_float(q.y & 0xFFFF0000u);
+  } else {
+#pragma unroll
+    for (int k = 0; k < V; ++k) v[k] = bf16_to_f32(p[i + k]);
+  }
+}
+template <int V>
+__device__ __forceinline__ void store_vec(float* p, int64_t i, const float (&v)[V]) {
+  if constexpr (V == 4) {
+    *reinterpret_cast<float4*>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < V; ++k) p[i + k] = v[k];
+  }
+}
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+template <int V>
+__device__ __forceinline__ void store_vec(bf16_bits* p, int64_t i, const float (&v)[V]) {
+  if constexpr (V == 4) {
+    *reinterpret_cast<uint2*>(p + i) = make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
+                                                  bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
+  } else {
+#pragma unroll
+    for (int k = 0; k < V; ++k) store_act(p, i + k, v[k]);
+  }
+}
+
+// Causal depthwise convolution of the x branch (with the variant's SiLU). Thread (channels
+// e0 .. e0 + V - 1, tokens t0 .. t0 + tpt - 1 of batch row b): the taps slide along the tokens in
+// registers, so each input is read once (plus a 3-token halo per run). The accumulation order
+// (bias, then taps oldest to newest) is the scan prologue's. Grid (ceil(E / (256 V)),
+// ceil(L / tpt), B); V = 4 needs E % 4 == 0.
+template <typename Act, bool kSilu, int V>
 __global__ __launch_bounds__(256) void conv_kernel(const Act* __restrict__ x,
                                                    const float* __restrict__ cache_in,
                                                    const float* __restrict__ w,
                                                    const float* __restrict__ bias,
-                                                   Act* __restrict__ u, int64_t B, int64_t L,
-                                                   int64_t E) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= B * L * E) return;
-  const int64_t e = i % E;
-  const int64_t t = (i / E) % L;
-  const int64_t b = i / (E * L);
-  float acc = bias[e];
+                                                   Act* __restrict__ u, int64_t L, int64_t E,
+                                                   int64_t tpt) {
+  const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * V;
+  if (e0 >= E) return;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * tpt;
+  const int64_t b = blockIdx.z;
+  float wk[V][kConv], bs[V];
 #pragma unroll
-  for (int k = 0; k < kConv; ++k) {
-    const int64_t tt = t - kHalo + k;
-    float xv;
-    if (tt >= 0)
-      xv = load_act(x, (b * L + tt) * E + e);
-    else
-      xv = cache_in ? cache_in[(b * kHalo + (tt + kHalo)) * E + e] : 0.0f;
-    acc = fmaf(w[e * kConv + k], xv, acc);
+  for (int v = 0; v < V; ++v) {
+    bs[v] = bias[e0 + v];
+#pragma unroll
+    for (int k = 0; k < kConv; ++k) wk[v][k] = w[(e0 + v) * kConv + k];
   }
-  if constexpr (kSilu) acc = silu(acc);
-  store_act(u, i, acc);
+  float win[kHalo][V];  // x[t - 3], x[t - 2], x[t - 1]
+#pragma unroll
+  for (int j = 0; j < kHalo; ++j) {
+    const int64_t tt = t0 - kHalo + j;
+    if (tt >= 0) {
+      load_vec<V>(x, (b * L + tt) * E + e0, win[j]);
+    } else {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        win[j][v] = cache_in ? cache_in[(b * kHalo + (tt + kHalo)) * E + e0 + v] : 0.0f;
+    }
+  }
+  const int64_t tend = t0 + tpt < L ? t0 + tpt : L;
+  for (int64_t t = t0; t < tend; ++t) {
+    float xv[V], out[V];
+    load_vec<V>(x, (b * L + t) * E + e0, xv);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      float acc = bs[v];
+      acc = fmaf(wk[v][0], win[0][v], acc);
+      acc = fmaf(wk[v][1], win[1][v], acc);
+      acc = fmaf(wk[v][2], win[2][v], acc);
+      acc = fmaf(wk[v][3], xv[v], acc);
+      if constexpr (kSilu) acc = silu(acc);
+      out[v] = acc;
+      win[0][v] = win[1][v];
+      win[1][v] = win[2][v];
+      win[2][v] = xv[v];
+    }
+    store_vec<V>(u, (b * L + t) * E + e0, out);
+  }
 }
 
 // conv_cache_out[b, j, e] = x~[b, L + j, e] for j < K-1 (the last K-1 entries of [cache_in, x]),
@@ -97,6 +173,34 @@ __global__ __launch_bounds__(256) void identity_conv_kernel(float* w, float* bia
 }
 
 unsigned blocks_for(int64_t n) { return static_cast<unsigned>((n + 255) / 256); }
+
+// Runs of 16 tokens per thread (longer when the sequence would need more than 65535 runs), four
+// channels per thread when d_inner allows 16-byte / 8-byte accesses.
+template <typename Act>
+void launch_conv(const Act* x, const float* cache_in, const float* w, const float* bias, Act* u,
+                 int64_t B, int64_t L, int64_t E, bool silu_conv, hipStream_t s) {
+  int64_t tpt = 16;
+  if ((L + tpt - 1) / tpt > 65535) tpt = (L + 65534) / 65535;
+  const unsigned gy = static_cast<unsigned>((L + tpt - 1) / tpt);
+  const dim3 blk(256);
+  if (E % 4 == 0) {
+    const dim3 grid(static_cast<unsigned>((E + 1023) / 1024), gy, static_cast<unsigned>(B));
+    if (silu_conv)
+      hipLaunchKernelGGL((conv_kernel<Act, true, 4>), grid, blk, 0, s, x, cache_in, w, bias, u, L,
+                         E, tpt);
+    else
+      hipLaunchKernelGGL((conv_kernel<Act, false, 4>), grid, blk, 0, s, x, cache_in, w, bias, u,
+                         L, E, tpt);
+  } else {
+    const dim3 grid(static_cast<unsigned>((E + 255) / 256), gy, static_cast<unsigned>(B));
+    if (silu_conv)
+      hipLaunchKernelGGL((conv_kernel<Act, true, 1>), grid, blk, 0, s, x, cache_in, w, bias, u, L,
+                         E, tpt);
+    else
+      hipLaunchKernelGGL((conv_kernel<Act, false, 1>), grid, blk, 0, s, x, cache_in, w, bias, u,
+                         L, E, tpt);
+  }
+}
 
 // Row-major C (M x N) = A (M x K) * W^T, W (N x K): in column-major terms C^T = W^T' * A^T',
 // i.e. op(A) = T on W stored K x N and op(B) = N on A stored K x M.
@@ -268,24 +372,14 @@ axon_status axon_layer_forward(axon_layer_ctx* ctx, const axon_layer_shape* shap
   const bool silu_conv = weights->ssm.conv_activation == AXON_CONV_SILU;
   if (bf16) {
     const auto* xb = reinterpret_cast<const bf16_bits*>(ws + lp.xb);
-    auto* u = reinterpret_cast<bf16_bits*>(ws + lp.u);
-    if (silu_conv)
-      hipLaunchKernelGGL((conv_kernel<bf16_bits, true>), dim3(blocks_for(M * E)), dim3(256), 0, s,
-                         xb, conv_cache_in, cw, cb, u, B, L, E);
-    else
-      hipLaunchKernelGGL((conv_kernel<bf16_bits, false>), dim3(blocks_for(M * E)), dim3(256), 0,
-                         s, xb, conv_cache_in, cw, cb, u, B, L, E);
+    launch_conv(xb, conv_cache_in, cw, cb, reinterpret_cast<bf16_bits*>(ws + lp.u), B, L, E,
+                silu_conv, s);
     hipLaunchKernelGGL((cache_kernel<bf16_bits>), dim3(blocks_for(B * E)), dim3(256), 0, s, xb,
                        conv_cache_in, conv_cache_out, B, L, E);
   } else {
     const auto* xb = reinterpret_cast<const float*>(ws + lp.xb);
-    auto* u = reinterpret_cast<float*>(ws + lp.u);
-    if (silu_conv)
-      hipLaunchKernelGGL((conv_kernel<float, true>), dim3(blocks_for(M * E)), dim3(256), 0, s, xb,
-                         conv_cache_in, cw, cb, u, B, L, E);
-    else
-      hipLaunchKernelGGL((conv_kernel<float, false>), dim3(blocks_for(M * E)), dim3(256), 0, s,
-                         xb, conv_cache_in, cw, cb, u, B, L, E);
+    launch_conv(xb, conv_cache_in, cw, cb, reinterpret_cast<float*>(ws + lp.u), B, L, E,
+                silu_conv, s);
     hipLaunchKernelGGL((cache_kernel<float>), dim3(blocks_for(B * E)), dim3(256), 0, s, xb,
                        conv_cache_in, conv_cache_out, B, L, E);
   }
