@@ -1,6 +1,7 @@
 """The size limits the C ABI accepts, run on the GPU: d_inner at its maximum (2^23 channels) and
 batch at its maximum (65535 rows), for prefill and for the decode step, compared with the oracle
-(sampled channels at 2^23, every channel at 65535 rows). One past each limit is rejected before
+(sampled channels at 2^23, every channel at 65535 rows); the SSD core at 65535 heads and at 65535
+batch rows. One past each limit is rejected before
 any launch; that is checked on the CPU in test_abi_cpu.py."""
 from __future__ import annotations
 
@@ -78,3 +79,32 @@ def test_max_batch_prefill_and_decode():
     assert_close(got, ref["y"], TOL["bf16"], "y (prefill + decode)")
     assert_close(host(state), ref["ssm_state"], STATE_TOL["bf16"], "state")
     np.testing.assert_array_equal(host(cache), ref["conv_cache"])
+
+
+def _ssd_limit_case(B, L, H, seed):
+    import workloads
+
+    w = workloads.SsdWorkload(9, "limit", B, L, H, "f32")
+    inp = workloads.ssd_inputs(w, seed_offset=seed)
+    dev = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).cuda()
+           for k in ("x", "dt_raw", "B", "C", "A_log", "D", "dt_bias")}
+    return inp, dev
+
+
+@pytest.mark.parametrize("B,H", [(1, MAX_BATCH), (MAX_BATCH, 1)])
+def test_ssd_max_heads_and_batch(B, H):
+    """The SSD core at 65535 heads, and at 65535 batch rows (3 tokens, incoming state), every
+    output compared with the oracle."""
+    import selective_state_space_depthwise_amd as axon
+
+    L = 3
+    say(f"[limits] ssd B={B} H={H} L={L}")
+    inp, d = _ssd_limit_case(B, L, H, seed=B + H)
+    sin = np.random.default_rng(93).standard_normal((B, H, 64, 128)).astype(np.float32)
+    y, st = axon.ssd_scan(d["x"], d["dt_raw"], d["B"], d["C"], d["A_log"], d["D"], d["dt_bias"],
+                          dt_min=inp["dt_min"], dt_max=inp["dt_max"],
+                          state_in=torch.from_numpy(sin).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.ssd_scan(inp, state_in=sin, threads=16)
+    assert_close(host(y), ref["y"], TOL["f32"], "ssd y")
+    assert_close(host(st), ref["ssm_state"], STATE_TOL["f32"], "ssd state")
