@@ -1,8 +1,8 @@
 """The size limits the C ABI accepts, run on the GPU: d_inner at its maximum (2^23 channels) and
 batch at its maximum (65535 rows), for prefill and for the decode step, compared with the oracle
 (sampled channels at 2^23, every channel at 65535 rows); the SSD core at 65535 heads and at 65535
-batch rows. One past each limit is rejected before
-any launch; that is checked on the CPU in test_abi_cpu.py."""
+batch rows. One past each limit is rejected before any launch; that is checked on the CPU in
+test_abi_cpu.py."""
 from __future__ import annotations
 
 import numpy as np
