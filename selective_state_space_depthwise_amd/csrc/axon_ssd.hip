@@ -27,10 +27,8 @@
 // assignment of the contraction index to (k-step, g) works as long as A and B use the same one.
 #include <hip/hip_runtime.h>
 
-#include <cstdint>
 #include <cmath>
-#include <cstring>
-#include <new>
+#include <cstdint>
 
 #include "axon_device.h"
 #include "axonscan.h"
