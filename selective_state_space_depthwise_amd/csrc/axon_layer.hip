@@ -254,7 +254,8 @@ bool shape_ok(const axon_layer_shape* s) {
   return s && s->batch >= 1 && s->seqlen >= 1 && s->d_model >= 1 && s->d_inner >= 1 &&
          s->d_inner <= kMaxChannels && s->batch <= 65535 && s->d_state == kState &&
          s->d_conv == kConv && (s->act_dtype == AXON_F32 || s->act_dtype == AXON_BF16) &&
-         s->batch * s->seqlen <= (int64_t(1) << 31) && s->d_model <= (int64_t(1) << 24);
+         s->seqlen <= (int64_t(1) << 31) && s->batch * s->seqlen <= (int64_t(1) << 31) &&
+         s->d_model <= (int64_t(1) << 24);
 }
 
 LayerPlan plan_layer(const axon_layer_shape* s) {

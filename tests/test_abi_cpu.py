@@ -200,6 +200,7 @@ def test_layer_workspace_is_a_pure_function_of_shape():
     assert A.layer_workspace_bytes(_lshape(seqlen=64)) > a
     assert A.layer_workspace_bytes(_lshape(d_state=8)) == 0
     assert A.layer_workspace_bytes(_lshape(seqlen=0)) == 0
+    assert A.layer_workspace_bytes(_lshape(batch=4, seqlen=1 << 62)) == 0  # batch * seqlen overflow
 
 
 _FAKE_CTX = ctypes.create_string_buffer(4096)  # zeroed host memory: a context with no handle
