@@ -110,3 +110,31 @@ def test_variant_full_size_axon_shape(conv_act, disc):
         assert_close(host(y[b, :, e]), ref["y"], TOL["f32"], f"y[{b},:,{e}]")
         assert_close(host(state[b, e]), ref["ssm_state"], STATE_TOL["f32"], f"state[{b},{e}]")
         np.testing.assert_array_equal(host(cache[b, :, e]), ref["conv_cache"])
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_long_stream_in_chunks(act):
+    """A long stream fed in pieces, as the streaming loop of "Selective State Space Models
+    (Mamba)" (pattern "1M context inference") does: 8 prefills of 1000 tokens (the time-chunked
+    path inside each), the Mamba-block variant (SiLU after the conv), caches carried in place
+    between calls; every output compared with one oracle pass over all 8000 tokens."""
+    B, L, E, n = 2, 8000, 192, 8
+    inp, extra = make_case(B, L, E, act, seed=61, caches=True)
+    _with(inp, "silu", "first_order")
+    say(f"[parity] long stream {B}x{L}x{E} {act} in {n} pieces")
+    d = to_device(inp)
+    cache = torch.from_numpy(extra["conv_cache_in"]).cuda()
+    state = torch.from_numpy(extra["ssm_state_in"]).cuda()
+    ys = []
+    step = L // n
+    for p in range(n):
+        part = {k: (v[:, p * step:(p + 1) * step].contiguous()
+                    if k in ("x", "z", "dt_raw", "B", "C") else v) for k, v in d.items()}
+        y, _, _ = gpu_prefill(part, conv_cache_in=cache, ssm_state_in=state,
+                              conv_cache_out=cache, ssm_state_out=state, conv_activation="silu")
+        ys.append(host(y))
+    torch.cuda.synchronize()
+    ref = oracle.prefill(inp, threads=8, **extra)
+    assert_close(np.concatenate(ys, axis=1), ref["y"], TOL[act], "streamed y")
+    assert_close(host(state), ref["ssm_state"], STATE_TOL[act], "streamed state")
+    np.testing.assert_array_equal(host(cache), ref["conv_cache"])
