@@ -109,6 +109,8 @@ def main():
                     help="time the whole layer (projections + path) with this d_model instead")
     ap.add_argument("--ssd", default="", metavar="WORKLOAD",
                     help="time the Mamba-2 SSD core instead (e.g. mamba2_ssd_f32_b1_l2048_h64)")
+    ap.add_argument("--micro", action="store_true",
+                    help="run only the instruction and HBM microbenchmarks (libaxonmicro.so)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 counters), if present")
     args = ap.parse_args()
@@ -123,6 +125,9 @@ def main():
         args.steps = wl.decode_steps if wl is not None and wl.kind == "decode" else 50
     if args.calibrate_copy:
         calibrate_copy(args.steps)
+        return
+    if args.micro:
+        bench_micro()
         return
 
     import torch
@@ -499,6 +504,66 @@ def bench_ssd(args, w):
             "kind": "oracle", "sample": f"first {Ls} tokens of the workload, all {H} heads, "
                                         f"{passes} passes in {el:.1f} s, double precision"}
     print(json.dumps(line), flush=True)
+
+
+MICRO_KINDS = ["fma", "exp", "dpp_row_newbcast_mul", "permlane32_swap", "state_update_mix",
+               "exp_1_per_4_fma", "fma_plus_salu", "fma_dependent_chain", "exp_dependent_chain",
+               "permlane16_swap", "exp_1_per_1_fma", "exp_1_per_2_fma", "exp_1_per_8_fma",
+               "lane_per_channel_update", "lane_per_channel_update_exp_as_mul",
+               "16_exp_then_48_fma", "8_exp_then_24_fma_twice", "16_exp_then_48_fma_vop3"]
+
+
+def bench_micro():
+    """Issue cost per wave64 instruction on one SIMD (cycles at the clock measured in the kernel
+    and at the nominal 2.4 GHz) for 1, 2 and 4 waves per SIMD, and HBM GB/s of a plain copy and a
+    plain read (libaxonmicro.so). One JSON line."""
+    import ctypes
+
+    from selective_state_space_depthwise_amd import build as _b
+
+    if not os.path.exists(_b.MICRO_LIB):
+        raise RuntimeError(f"{_b.MICRO_LIB} is missing: run python -m "
+                           "selective_state_space_depthwise_amd.build")
+    lib = ctypes.CDLL(_b.MICRO_LIB)
+    lib.axon_micro_alu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.POINTER(ctypes.c_double)]
+    lib.axon_micro_hbm.argtypes = [ctypes.c_int, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                   ctypes.POINTER(ctypes.c_double)]
+    simds = 256 * 4
+    out = (ctypes.c_double * 3)()
+    alu = {}
+    clock_ghz = []
+    for kind, name in enumerate(MICRO_KINDS):
+        per = lib.axon_micro_alu_instrs_per_iter(kind)
+        alu[name] = {}
+        for wps in (1, 2, 4):
+            iters = 2000
+            rc = lib.axon_micro_alu(kind, wps, iters, out)
+            if rc:
+                raise RuntimeError(f"micro {name} wps {wps}: hip error {rc}")
+            ms, tick, rtick = out[0], out[1], out[2]
+            ghz = tick / (rtick / 100e6) / 1e9 if rtick else float("nan")
+            clock_ghz.append(ghz)
+            instrs = iters * per * wps  # wave64 instructions issued per SIMD
+            ns = ms * 1e6 / instrs
+            alu[name][f"{wps}_wave_per_simd"] = {
+                "ns_per_instr": round(ns, 4), "cycles_at_2.4GHz": round(ns * 2.4, 3),
+                "cycles_at_measured_clock": round(ns * ghz, 3), "ms": round(ms, 4)}
+        print(f"micro {name} done", file=sys.stderr, flush=True)
+    hbm = {}
+    for kind, name in ((0, "copy"), (1, "read")):
+        nbytes = 1 << 30
+        for blocks in (2048, 8192):
+            rc = lib.axon_micro_hbm(kind, nbytes, 10, blocks, out)
+            if rc:
+                raise RuntimeError(f"micro hbm {name}: hip error {rc}")
+            moved = nbytes * (2 if kind == 0 else 1)
+            hbm[f"{name}_{blocks}_workgroups"] = {
+                "GB_per_s": round(moved / (out[0] / 1e3) / 1e9, 1), "ms": round(out[0], 4),
+                "bytes_moved": moved}
+    print(json.dumps({"micro": "gfx950 instruction issue and HBM streaming",
+                      "s_memtime_clock_GHz": round(float(np.median(clock_ghz)), 4),
+                      "simds": simds, "alu": alu, "hbm": hbm}), flush=True)
 
 
 def _kernel_source_sha():

@@ -1,4 +1,5 @@
-"""Build libaxonscan.so in-tree: the HIP kernels with hipcc for gfx950, the C-ABI layer with g++.
+"""Build libaxonscan.so in-tree: the HIP kernels with hipcc for gfx950, the C-ABI layer with g++;
+and libaxonmicro.so, the instruction and bandwidth microbenchmarks.
 
 Usage: python -m selective_state_space_depthwise_amd.build
 """
@@ -15,8 +16,13 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libaxonscan.so")
+# Microbenchmarks of the instructions the kernels are built from (bench.py --micro); a library
+# of its own so the product library carries none of it.
+MICRO_SOURCE = "axon_microbench.hip"
+MICRO_LIB = os.path.join(PKG, "libaxonmicro.so")
 
-HIP_SOURCES = ["axon_kernels.hip", "axon_rowscan.hip", "axon_layer.hip", "axon_ssd.hip"]
+HIP_SOURCES = ["axon_kernels.hip", "axon_rowscan.hip", "axon_chanscan.hip", "axon_layer.hip",
+               "axon_ssd.hip"]
 CXX_SOURCES = ["axonscan_api.cpp"]
 ARCH = "gfx950"
 ROCM_LIB = "/opt/rocm/lib"  # hipBLASLt (the layer's projection GEMMs)
@@ -57,6 +63,10 @@ def build(verbose: bool = False) -> str:
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs,
           f"-L{ROCM_LIB}", "-lhipblaslt", f"-Wl,-rpath,{ROCM_LIB}"], verbose)
     os.replace(tmp, LIB)
+    tmp = MICRO_LIB + f".tmp{os.getpid()}"
+    _run([hipcc, *HIP_FLAGS, "-shared", "-I", CSRC, os.path.join(CSRC, MICRO_SOURCE), "-o", tmp],
+         verbose)
+    os.replace(tmp, MICRO_LIB)
     return LIB
 
 

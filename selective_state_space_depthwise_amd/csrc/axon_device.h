@@ -71,6 +71,32 @@ __device__ __forceinline__ float load_buf<bf16_bits>(rsrc_t r, uint32_t off) {
   return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
 }
 
+// The same with a wave-uniform byte offset added (soffset).
+template <typename Act>
+__device__ __forceinline__ float load_buf_s(rsrc_t r, uint32_t off, uint32_t soff);
+template <>
+__device__ __forceinline__ float load_buf_s<float>(rsrc_t r, uint32_t off, uint32_t soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
+}
+template <>
+__device__ __forceinline__ float load_buf_s<bf16_bits>(rsrc_t r, uint32_t off, uint32_t soff) {
+  return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0));
+}
+
+template <typename Act>
+__device__ __forceinline__ void store_buf_s(rsrc_t r, uint32_t off, uint32_t soff, float v);
+template <>
+__device__ __forceinline__ void store_buf_s<float>(rsrc_t r, uint32_t off, uint32_t soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, soff, 0);
+}
+template <>
+__device__ __forceinline__ void store_buf_s<bf16_bits>(rsrc_t r, uint32_t off, uint32_t soff,
+                                                       float v) {
+  uint32_t u = __float_as_uint(v);  // round to nearest, ties to even
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(u >> 16), r, off, soff, 0);
+}
+
 template <typename Act>
 __device__ __forceinline__ void store_buf(rsrc_t r, uint32_t off, float v);
 template <>

@@ -20,7 +20,13 @@ constexpr int kHalo = kConv - 1;
 // state and keeps its carry (sum of dt, local final state); a small combine pass turns the
 // carries into each chunk's true initial state; the final pass re-scans each chunk from that
 // state and writes the outputs.
+enum PrefillKernel : int {
+  kRowScan = 0,   // 16 states of a channel spread over lanes (axon_rowscan.hip)
+  kChanScan = 1,  // one lane per channel, 16 states in its registers (axon_chanscan.hip)
+};
+
 struct PrefillPlan {
+  int kernel = kRowScan;
   int row_waves = 2;      // W: waves per 16-channel group (states per lane = 4 / W)
   int64_t chunks = 1;     // M
   int64_t chunk_len = 0;  // T (tokens per chunk; the last chunk may be shorter)
@@ -64,6 +70,7 @@ int launch_prefill(const PrefillLaunch& a, const PrefillPlan& plan, void* stream
 axon_status validate_params(const axon_ssm_params* p);
 constexpr int64_t kMaxChannels = int64_t(1) << 23;  // d_inner limit of the prefill kernels
 int launch_row_scan(const PrefillLaunch& a, const PrefillPlan& plan, void* stream);
+int launch_chan_scan(const PrefillLaunch& a, const PrefillPlan& plan, void* stream);
 int launch_decode(const DecodeLaunch& a, void* stream);
 
 }  // namespace axon

@@ -12,7 +12,10 @@ namespace {
 
 // Carry combine of the time-chunked prefill: one thread per (b, e, n) walks the M chunks in
 // order, H_0 = state_in, H_{c+1} = exp(A S_c) H_c + h_c, where S_c is the chunk's sum of dt
-// (the product of the chunk's decays exp(dt A)) and h_c its local final state from zero.
+// (the product of the chunk's decays exp(dt A)) and h_c its local final state from zero. The
+// carries of eight chunks are loaded before they are folded, so the loads of a group overlap.
+constexpr int kCombineGroup = 8;
+
 __global__ __launch_bounds__(256) void carry_combine_kernel(int64_t B, int64_t E, int64_t M,
                                                             const float* __restrict__ A_log,
                                                             const float* __restrict__ state_in,
@@ -27,11 +30,22 @@ __global__ __launch_bounds__(256) void carry_combine_kernel(int64_t B, int64_t E
   const int64_t n = idx % kState;
   const float rate = decay_rate_log2(A_log[e * kState + n]);
   float H = state_in ? state_in[idx] : 0.0f;
-  for (int64_t c = 0; c < M; ++c) {
-    carry_in[c * total + idx] = H;
-    if (c + 1 < M) {
-      const float decay = __builtin_amdgcn_exp2f(rate * carry_s[c * B * E + be]);
-      H = fmaf(decay, H, carry_h[c * total + idx]);
+  carry_in[idx] = H;
+  // chunks 0..M-2 carry into 1..M-1
+  for (int64_t c0 = 0; c0 + 1 < M; c0 += kCombineGroup) {
+    float hc[kCombineGroup], sc[kCombineGroup];
+#pragma unroll
+    for (int i = 0; i < kCombineGroup; ++i) {
+      const int64_t c = c0 + i < M - 1 ? c0 + i : M - 2;
+      hc[i] = carry_h[c * total + idx];
+      sc[i] = carry_s[c * B * E + be];
+    }
+#pragma unroll
+    for (int i = 0; i < kCombineGroup; ++i) {
+      if (c0 + i + 1 < M) {
+        H = fmaf(__builtin_amdgcn_exp2f(rate * sc[i]), H, hc[i]);
+        carry_in[(c0 + i + 1) * total + idx] = H;
+      }
     }
   }
 }
@@ -195,7 +209,8 @@ int launch_prefill(const PrefillLaunch& p, const PrefillPlan& plan, void* stream
     }
     return static_cast<int>(hipGetLastError());
   }
-  return launch_row_scan(p, plan, stream);
+  return plan.kernel == kChanScan ? launch_chan_scan(p, plan, stream)
+                                  : launch_row_scan(p, plan, stream);
 }
 
 int launch_decode(const DecodeLaunch& p, void* stream) {

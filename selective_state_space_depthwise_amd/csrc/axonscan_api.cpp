@@ -33,6 +33,18 @@ constexpr int64_t kTwoStateChannels = 16384;
 constexpr int64_t kTargetLanes = 524288;
 constexpr int64_t kMinChunk = 256;
 constexpr int64_t kMaxChunks = 64;
+// Lane-per-channel scan: time chunks up to about kChanTargetLanes lanes in the final pass, with
+// chunks of at least kChanMinChunk tokens.
+#ifndef AXON_PLAN_KERNEL
+#define AXON_PLAN_KERNEL 2
+#endif
+#ifndef AXON_CHAN_TARGET_LANES
+#define AXON_CHAN_TARGET_LANES 524288
+#endif
+constexpr int kPlanKernel = AXON_PLAN_KERNEL;  // 0: row scan only, 1: lane per channel only, 2: by shape
+constexpr int64_t kChanTargetLanes = AXON_CHAN_TARGET_LANES;
+constexpr int64_t kChanMinChunk = 64;
+constexpr int64_t kChanMaxChunks = 256;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -104,9 +116,52 @@ namespace axon {
 
 axon_status validate_params(const axon_ssm_params* p) { return check_params(p); }
 
+namespace {
+
+void layout_workspace(PrefillPlan& plan, int64_t channels) {
+  if (plan.chunks <= 1) return;
+  const int64_t M = plan.chunks;
+  const size_t be = static_cast<size_t>(channels);
+  size_t off = 0;
+  plan.off_carry_h = off;
+  off = round_up(off + sizeof(float) * M * be * kState, 256);
+  plan.off_carry_s = off;
+  off = round_up(off + sizeof(float) * M * be, 256);
+  plan.off_carry_in = off;
+  off = round_up(off + sizeof(float) * M * be * kState, 256);
+  plan.off_halo = off;
+  off = round_up(off + sizeof(float) * be * kHalo, 256);
+  plan.workspace_bytes = off;
+}
+
+// Chunk length for M chunks: whole unrolled steps (8 tokens) where the sequence allows.
+void set_chunks(PrefillPlan& plan, int64_t seqlen, int64_t M, int64_t step) {
+  if (M < 1) M = 1;
+  int64_t T = (seqlen + M - 1) / M;
+  T = (T + step - 1) / step * step;
+  if (T < step) T = step;
+  plan.chunks = (seqlen + T - 1) / T;
+  if (plan.chunks < 1) plan.chunks = 1;
+  plan.chunk_len = T;
+}
+
+}  // namespace
+
 PrefillPlan plan_prefill(int64_t batch, int64_t seqlen, int64_t d_inner) {
   PrefillPlan plan;
   const int64_t channels = batch * d_inner;
+  const bool chan = kPlanKernel == 1 || (kPlanKernel == 2 && channels < kSinglePassChannels);
+  if (chan) {
+    plan.kernel = kChanScan;
+    int64_t M = (kChanTargetLanes + channels - 1) / channels;
+    int64_t max_m = seqlen / kChanMinChunk;
+    if (max_m < 1) max_m = 1;
+    if (M > max_m) M = max_m;
+    if (M > kChanMaxChunks) M = kChanMaxChunks;
+    set_chunks(plan, seqlen, M, 8);
+    layout_workspace(plan, channels);
+    return plan;
+  }
   const bool single_pass = channels >= kSinglePassChannels;
   plan.row_waves = single_pass && channels < kTwoStateChannels ? 4 : 2;
   const int64_t lanes = channels * 4 * plan.row_waves;
@@ -119,27 +174,8 @@ PrefillPlan plan_prefill(int64_t batch, int64_t seqlen, int64_t d_inner) {
     if (M > kMaxChunks) M = kMaxChunks;
   }
   // Chunks hold whole scan tiles (32 tokens with one state per lane, else 16).
-  const int64_t tile = plan.row_waves == 4 ? 32 : 16;
-  int64_t T = (seqlen + M - 1) / M;
-  T = (T + tile - 1) / tile * tile;
-  if (T < tile) T = tile;
-  M = (seqlen + T - 1) / T;
-  if (M < 1) M = 1;
-  plan.chunks = M;
-  plan.chunk_len = T;
-  if (M > 1) {
-    const size_t be = static_cast<size_t>(channels);
-    size_t off = 0;
-    plan.off_carry_h = off;
-    off = round_up(off + sizeof(float) * M * be * kState, 256);
-    plan.off_carry_s = off;
-    off = round_up(off + sizeof(float) * M * be, 256);
-    plan.off_carry_in = off;
-    off = round_up(off + sizeof(float) * M * be * kState, 256);
-    plan.off_halo = off;
-    off = round_up(off + sizeof(float) * be * kHalo, 256);
-    plan.workspace_bytes = off;
-  }
+  set_chunks(plan, seqlen, M, plan.row_waves == 4 ? 32 : 16);
+  layout_workspace(plan, channels);
   return plan;
 }
 
