@@ -195,14 +195,29 @@ void axon_layer_destroy(axon_layer_ctx* ctx);
 size_t axon_layer_workspace_bytes(const axon_layer_shape* shape);
 
 /* Forward over seqlen tokens: x_in (B, L, D) -> out (B, L, D), continuing from the caches as
- * axon_ssm_prefill does (NULL inputs = zeros; outputs may equal the inputs, in place). out must
- * not overlap any input, weight or cache; workspace: axon_layer_workspace_bytes(shape) bytes,
+ * axon_ssm_prefill does (NULL inputs = zeros). Aliasing: out, the workspace, conv_cache_out and
+ * ssm_state_out must not overlap x_in, a weight, a parameter array or one another; out and the
+ * workspace also not the cache / state inputs; conv_cache_out may equal conv_cache_in and
+ * ssm_state_out may equal ssm_state_in exactly (in place), never overlap them partly; the cache
+ * output must not overlap the state input nor the state output the cache input. Any violation:
+ * AXON_ERR_INVALID_ARGUMENT, nothing written. workspace: axon_layer_workspace_bytes(shape) bytes,
  * 16-byte aligned, contents need no initialisation. */
 axon_status axon_layer_forward(axon_layer_ctx* ctx, const axon_layer_shape* shape,
                                const axon_layer_weights* weights, const void* x_in,
                                const float* conv_cache_in, const float* ssm_state_in, void* out,
                                float* conv_cache_out, float* ssm_state_out, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* The checks axon_layer_forward makes of its arguments before it launches anything (shape,
+ * parameters, null and misaligned pointers, workspace size, aliasing), without a context and
+ * without touching device memory: AXON_OK when the forward call with these arguments would run.
+ * Pointers are only compared, never dereferenced. */
+axon_status axon_layer_forward_check(const axon_layer_shape* shape,
+                                     const axon_layer_weights* weights, const void* x_in,
+                                     const float* conv_cache_in, const float* ssm_state_in,
+                                     const void* out, const float* conv_cache_out,
+                                     const float* ssm_state_out, const void* workspace,
+                                     size_t workspace_bytes);
 
 /* ---- Mamba-2 SSD core ------------------------------------------------------------------------
  * The state space duality (SSD) layer core of Mamba-2 ["Selective State Space Models (Mamba)",

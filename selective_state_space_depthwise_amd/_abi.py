@@ -109,6 +109,10 @@ def load():
         lib.axon_layer_forward.argtypes = [
             P, ctypes.POINTER(LayerShape), ctypes.POINTER(LayerWeights), P, P, P, P, P, P, P,
             ctypes.c_size_t, P]
+        lib.axon_layer_forward_check.restype = ctypes.c_int
+        lib.axon_layer_forward_check.argtypes = [
+            ctypes.POINTER(LayerShape), ctypes.POINTER(LayerWeights), P, P, P, P, P, P, P,
+            ctypes.c_size_t]
         lib.axon_ssd_scan_workspace_bytes.restype = ctypes.c_size_t
         lib.axon_ssd_scan_workspace_bytes.argtypes = [ctypes.POINTER(SsdShape)]
         lib.axon_ssd_scan.restype = ctypes.c_int
@@ -188,6 +192,15 @@ def raw_layer_forward(ctx, shape: LayerShape, weights: LayerWeights, x_in, cache
     return load().axon_layer_forward(ctx, ctypes.byref(shape), ctypes.byref(weights), x_in,
                                      cache_in, state_in, out, cache_out, state_out, workspace,
                                      int(workspace_bytes_), stream)
+
+
+def raw_layer_forward_check(shape: LayerShape, weights: LayerWeights, x_in, cache_in, state_in,
+                            out, cache_out, state_out, workspace, workspace_bytes_) -> int:
+    """axon_layer_forward_check with integer pointers (compared only, never dereferenced).
+    Returns the status code axon_layer_forward would give these arguments before launching."""
+    return load().axon_layer_forward_check(ctypes.byref(shape), ctypes.byref(weights), x_in,
+                                           cache_in, state_in, out, cache_out, state_out,
+                                           workspace, int(workspace_bytes_))
 
 
 def make_ssd_shape(batch, seqlen, n_heads, act_bf16, head_dim=64, d_state=128) -> SsdShape:

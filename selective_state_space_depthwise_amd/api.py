@@ -20,6 +20,17 @@ def _stream_handle(device, stream):
     return s.cuda_stream
 
 
+def _keep_for(device, stream, *tensors):
+    """Tensors this binding allocated (from torch's caching allocator, on the current stream) and
+    hands to kernels launched on another stream: record that stream on them, so that when they
+    are freed their memory is not handed out again before the work queued on it has run."""
+    if stream is None or stream == torch.cuda.current_stream(device):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def _act_dtype(x: torch.Tensor) -> bool:
     if x.dtype == torch.float32:
         return False
@@ -88,19 +99,25 @@ def prefill(x, z, dt_raw, B, C, A_log, D, dt_bias, conv_w, conv_b, *, dt_min=1e-
         _check(conv_cache_in, "conv_cache_in", cache_shape, torch.float32, device)
     if ssm_state_in is not None:
         _check(ssm_state_in, "ssm_state_in", state_shape, torch.float32, device)
+    mine = []  # tensors allocated here
     if y is None:
         y = torch.empty_like(x)
+        mine.append(y)
     _check(y, "y", (Bsz, L, E), x.dtype, device)
     if conv_cache_out is None:
         conv_cache_out = torch.empty(cache_shape, dtype=torch.float32, device=device)
+        mine.append(conv_cache_out)
     if ssm_state_out is None:
         ssm_state_out = torch.empty(state_shape, dtype=torch.float32, device=device)
+        mine.append(ssm_state_out)
     _check(conv_cache_out, "conv_cache_out", cache_shape, torch.float32, device)
     _check(ssm_state_out, "ssm_state_out", state_shape, torch.float32, device)
     shape = _abi.make_shape(Bsz, L, E, bf16)
     need = _abi.workspace_bytes(shape)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        mine.append(workspace)
+    _keep_for(device, stream, *mine)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = _abi.raw_prefill(
@@ -136,6 +153,7 @@ def decode_step(x, z, dt_raw, B, C, A_log, D, dt_bias, conv_w, conv_b, conv_cach
     _check(ssm_state, "ssm_state", (Bsz, E, D_STATE), torch.float32, device)
     if y is None:
         y = torch.empty_like(x)
+        _keep_for(device, stream, y)
     _check(y, "y", (Bsz, E), x.dtype, device)
     st = _abi.raw_decode_step(
         _abi.make_shape(Bsz, 1, E, bf16), prm, x.data_ptr(), z.data_ptr(), dt_raw.data_ptr(),
@@ -192,13 +210,17 @@ class Layer:
                       conv_activation, discretization)
         shape = _abi.make_layer_shape(Bsz, L, Dm, E, bf16)
         weights = _abi.LayerWeights(W_in.data_ptr(), W_f.data_ptr(), W_out.data_ptr(), prm)
+        mine = []
         if out is None:
             out = torch.empty_like(x_in)
+            mine.append(out)
         _check(out, "out", (Bsz, L, Dm), x_in.dtype, device)
         if conv_cache_out is None:
             conv_cache_out = torch.empty((Bsz, D_CONV - 1, E), dtype=torch.float32, device=device)
+            mine.append(conv_cache_out)
         if ssm_state_out is None:
             ssm_state_out = torch.empty((Bsz, E, D_STATE), dtype=torch.float32, device=device)
+            mine.append(ssm_state_out)
         for t, n, shp in ((conv_cache_in, "conv_cache_in", (Bsz, D_CONV - 1, E)),
                           (ssm_state_in, "ssm_state_in", (Bsz, E, D_STATE)),
                           (conv_cache_out, "conv_cache_out", (Bsz, D_CONV - 1, E)),
@@ -208,6 +230,9 @@ class Layer:
         need = _abi.layer_workspace_bytes(shape)
         if self._ws is None or self._ws.numel() < need or self._ws.device != device:
             self._ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        # the cached workspace is recorded on every stream that uses it, so that replacing it
+        # later does not free memory a kernel on that stream still uses
+        _keep_for(device, stream, self._ws, *mine)
         ptr = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
         st = _abi.raw_layer_forward(self._ctx, shape, weights, x_in.data_ptr(), ptr(conv_cache_in),
                                     ptr(ssm_state_in), out.data_ptr(), conv_cache_out.data_ptr(),
@@ -249,11 +274,14 @@ def ssd_scan(x, dt_raw, B, C, A_log, D, dt_bias, *, dt_min=1e-4, dt_max=100.0, s
     state_shape = (Bsz, H, SSD_HEAD_DIM, SSD_STATE)
     if state_in is not None:
         _check(state_in, "state_in", state_shape, torch.float32, device)
+    mine = []
     if y is None:
         y = torch.empty_like(x)
+        mine.append(y)
     _check(y, "y", tuple(x.shape), x.dtype, device)
     if state_out is None:
         state_out = torch.empty(state_shape, dtype=torch.float32, device=device)
+        mine.append(state_out)
     _check(state_out, "state_out", state_shape, torch.float32, device)
     shape = _abi.make_ssd_shape(Bsz, L, H, bf16)
     prm = _abi.SsdParams(A_log.data_ptr(), D.data_ptr(), dt_bias.data_ptr(), float(dt_min),
@@ -261,6 +289,8 @@ def ssd_scan(x, dt_raw, B, C, A_log, D, dt_bias, *, dt_min=1e-4, dt_max=100.0, s
     need = _abi.ssd_workspace_bytes(shape)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        mine.append(workspace)
+    _keep_for(device, stream, *mine)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = _abi.raw_ssd_scan(shape, prm, x.data_ptr(), dt_raw.data_ptr(), B.data_ptr(),

@@ -65,6 +65,24 @@ struct DecodeLaunch {
   void* y;
 };
 
+// Byte ranges of device buffers, for the aliasing checks of the entry points.
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+};
+inline Span span(const void* p, size_t bytes) {
+  Span s;
+  if (p && bytes) {
+    s.lo = reinterpret_cast<uintptr_t>(p);
+    s.hi = s.lo + bytes;
+  }
+  return s;
+}
+inline bool overlaps(const Span& a, const Span& b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+// Byte spans of a parameter block's arrays (read-only inputs), for d_inner = E.
+void param_spans(const axon_ssm_params* p, int64_t E, Span out[5]);
+
 int launch_prefill(const PrefillLaunch& a, const PrefillPlan& plan, void* stream);
 // The C-ABI checks of a parameter block (pointers, alignment, clips, variants).
 axon_status validate_params(const axon_ssm_params* p);

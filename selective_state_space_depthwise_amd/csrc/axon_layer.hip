@@ -316,13 +316,14 @@ size_t axon_layer_workspace_bytes(const axon_layer_shape* shape) {
   return axon::plan_layer(shape).total;
 }
 
-axon_status axon_layer_forward(axon_layer_ctx* ctx, const axon_layer_shape* shape,
-                               const axon_layer_weights* weights, const void* x_in,
-                               const float* conv_cache_in, const float* ssm_state_in, void* out,
-                               float* conv_cache_out, float* ssm_state_out, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+axon_status axon_layer_forward_check(const axon_layer_shape* shape,
+                                     const axon_layer_weights* weights, const void* x_in,
+                                     const float* conv_cache_in, const float* ssm_state_in,
+                                     const void* out, const float* conv_cache_out,
+                                     const float* ssm_state_out, const void* workspace,
+                                     size_t workspace_bytes) {
   using namespace axon;
-  if (!ctx || !weights || !shape) return AXON_ERR_INVALID_ARGUMENT;
+  if (!weights || !shape) return AXON_ERR_INVALID_ARGUMENT;
   if (shape->d_state != kState || shape->d_conv != kConv ||
       (shape->act_dtype != AXON_F32 && shape->act_dtype != AXON_BF16))
     return AXON_ERR_UNSUPPORTED;
@@ -337,20 +338,57 @@ axon_status axon_layer_forward(axon_layer_ctx* ctx, const axon_layer_shape* shap
     return AXON_ERR_INVALID_ARGUMENT;
   const LayerPlan lp = plan_layer(shape);
   if (workspace_bytes < lp.total) return AXON_ERR_WORKSPACE_TOO_SMALL;
-  // out overlaps neither the input activations nor the workspace.
+
+  // Aliasing: out, the workspace and the cache / state outputs overlap nothing they must not.
+  // A cache or state output may be its input exactly (in place), never partly.
+  const size_t elt = shape->act_dtype == AXON_BF16 ? 2 : 4;
+  const int64_t B = shape->batch, L = shape->seqlen, D = shape->d_model, E = shape->d_inner;
+  const size_t tok = static_cast<size_t>(B * L);
+  const Span s_x = span(x_in, tok * D * elt), s_out = span(out, tok * D * elt);
+  const Span s_win = span(weights->W_in, static_cast<size_t>(2 * E * D) * elt);
+  const Span s_wf = span(weights->W_f, static_cast<size_t>((2 * kState + E) * E) * elt);
+  const Span s_wout = span(weights->W_out, static_cast<size_t>(D * E) * elt);
+  const size_t cache_bytes = sizeof(float) * B * kHalo * E;
+  const size_t state_bytes = sizeof(float) * B * E * kState;
+  const Span s_cin = span(conv_cache_in, cache_bytes), s_sin = span(ssm_state_in, state_bytes);
+  const Span s_cout = span(conv_cache_out, cache_bytes), s_sout = span(ssm_state_out, state_bytes);
+  const Span s_ws = span(workspace, lp.total);
+  Span prm[5];
+  param_spans(&weights->ssm, E, prm);
+  const Span reads[] = {s_x, s_win, s_wf, s_wout, prm[0], prm[1], prm[2], prm[3], prm[4]};
+  for (const Span& r : reads) {
+    if (overlaps(s_out, r) || overlaps(s_cout, r) || overlaps(s_sout, r) || overlaps(s_ws, r))
+      return AXON_ERR_INVALID_ARGUMENT;
+  }
+  const Span others_of_out[] = {s_cin, s_sin, s_cout, s_sout, s_ws};
+  for (const Span& o : others_of_out)
+    if (overlaps(s_out, o)) return AXON_ERR_INVALID_ARGUMENT;
+  const Span others_of_ws[] = {s_cin, s_sin, s_cout, s_sout};
+  for (const Span& o : others_of_ws)
+    if (overlaps(s_ws, o)) return AXON_ERR_INVALID_ARGUMENT;
+  if (conv_cache_in != conv_cache_out && overlaps(s_cout, s_cin)) return AXON_ERR_INVALID_ARGUMENT;
+  if (ssm_state_in != ssm_state_out && overlaps(s_sout, s_sin)) return AXON_ERR_INVALID_ARGUMENT;
+  if (overlaps(s_cout, s_sout) || overlaps(s_cout, s_sin) || overlaps(s_sout, s_cin))
+    return AXON_ERR_INVALID_ARGUMENT;
+  return AXON_OK;
+}
+
+axon_status axon_layer_forward(axon_layer_ctx* ctx, const axon_layer_shape* shape,
+                               const axon_layer_weights* weights, const void* x_in,
+                               const float* conv_cache_in, const float* ssm_state_in, void* out,
+                               float* conv_cache_out, float* ssm_state_out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  using namespace axon;
+  if (!ctx) return AXON_ERR_INVALID_ARGUMENT;
+  const axon_status cst =
+      axon_layer_forward_check(shape, weights, x_in, conv_cache_in, ssm_state_in, out,
+                               conv_cache_out, ssm_state_out, workspace, workspace_bytes);
+  if (cst != AXON_OK) return cst;
+  const LayerPlan lp = plan_layer(shape);
   const bool bf16 = shape->act_dtype == AXON_BF16;
   const size_t elt = bf16 ? 2 : 4;
   const int64_t B = shape->batch, L = shape->seqlen, D = shape->d_model, E = shape->d_inner;
   const int64_t M = B * L;
-  {
-    const char* o = static_cast<const char*>(out);
-    const size_t ob = static_cast<size_t>(M * D) * elt;
-    auto hits = [&](const void* p, size_t n) {
-      const char* c = static_cast<const char*>(p);
-      return c < o + ob && o < c + n;
-    };
-    if (hits(x_in, ob) || hits(workspace, lp.total)) return AXON_ERR_INVALID_ARGUMENT;
-  }
 
   if (!ctx->blas) return AXON_ERR_INVALID_ARGUMENT;  // the context is used only past here
 

@@ -48,22 +48,10 @@ constexpr int64_t kChanMaxChunks = 256;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-struct Span {
-  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
-};
-
-Span span(const void* p, size_t bytes) {
-  Span s;
-  if (p && bytes) {
-    s.lo = reinterpret_cast<uintptr_t>(p);
-    s.hi = s.lo + bytes;
-  }
-  return s;
-}
-
-bool overlaps(const Span& a, const Span& b) {
-  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
-}
+using axon::overlaps;
+using axon::param_spans;
+using axon::span;
+using axon::Span;
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return !__builtin_mul_overflow(a, b, out) && *out <= kMaxElems;
@@ -101,18 +89,17 @@ axon_status check_params(const axon_ssm_params* p) {
   return AXON_OK;
 }
 
-// Byte spans of the parameter arrays (read-only inputs).
-void param_spans(const axon_ssm_params* p, int64_t E, Span out[5]) {
-  out[0] = span(p->A_log, sizeof(float) * E * axon::kState);
-  out[1] = span(p->D, sizeof(float) * E);
-  out[2] = span(p->dt_bias, sizeof(float) * E);
-  out[3] = span(p->conv_w, sizeof(float) * E * axon::kConv);
-  out[4] = span(p->conv_b, sizeof(float) * E);
-}
-
 }  // namespace
 
 namespace axon {
+
+void param_spans(const axon_ssm_params* p, int64_t E, Span out[5]) {
+  out[0] = span(p->A_log, sizeof(float) * E * kState);
+  out[1] = span(p->D, sizeof(float) * E);
+  out[2] = span(p->dt_bias, sizeof(float) * E);
+  out[3] = span(p->conv_w, sizeof(float) * E * kConv);
+  out[4] = span(p->conv_b, sizeof(float) * E);
+}
 
 axon_status validate_params(const axon_ssm_params* p) { return check_params(p); }
 

@@ -5,10 +5,14 @@ Tolerances (element-wise, against the oracle run on the same rounded inputs):
   fp32 activations: |gpu - ref| <= 1e-4 * (1 + |ref|)
   bf16 activations: |gpu - ref| <= 2e-2 * (1 + |ref|)   (y is rounded to bf16; state stays fp32)
   conv cache: bit-exact (it holds copies of the inputs).
-Stress cases outside the workloads' distributions (fp32 with dt clipped at 50..100, where the
-states grow to ~100 and an output can be the small difference of large terms) use
-  |gpu - ref| <= 1e-4 * (1 + |ref| + mag),  mag = |SiLU(z)| * (sum_n |C h_n| + |D u|)
-from the oracle: fp32 rounding of the summed terms alone is of order 1e-7 * mag.
+The fp32 stress cases with dt spanning [1e-4, 1] plus clip hits ("wide": states reach
+thousands and an output can be the small difference of large terms) add a term for the size
+of what each output sums:
+  |gpu - ref| <= 1e-4 * (1 + |ref|) + MAG_TOL * mag,  mag = |SiLU(z)| (sum_n |C h_n| + |D u|)
+(``mag`` from the oracle, pinned to the LTI closed form). MAG_TOL = 1e-5: with dt >= 1e-4 and
+|A| >= 1 a state remembers at most 1e4 steps, each adding one fp32 rounding (2^-24) to a running
+sum; independent roundings grow as the square root of their count, sqrt(1e4) * 2^-24 = 6e-6 of
+the terms' size, and 1e-5 leaves a margin over that.
 """
 from __future__ import annotations
 
@@ -21,6 +25,7 @@ import oracle
 import workloads
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+MAG_TOL = 1e-5
 # The state is fp32 in both cases; for bf16 runs its error is set by the same fp32 arithmetic.
 STATE_TOL = {"f32": 1e-4, "bf16": 1e-4}
 ACT_KEYS = ("x", "z", "dt_raw", "B", "C")
@@ -79,7 +84,9 @@ def assert_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str, mag=No
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite values from the GPU"
     err = np.abs(got - ref)
-    bound = tol * (1.0 + np.abs(ref) + (0.0 if mag is None else np.asarray(mag, np.float64)))
+    bound = tol * (1.0 + np.abs(ref))
+    if mag is not None:
+        bound = bound + MAG_TOL * np.asarray(mag, np.float64)
     bad = err > bound
     if bad.any():
         idx = np.unravel_index(np.argmax(err / bound), err.shape)
@@ -92,36 +99,6 @@ def max_rel(got, ref) -> float:
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     return float(np.max(np.abs(got - ref) / (1.0 + np.abs(ref)))) if got.size else 0.0
-
-
-def sample_channels(Bsz: int, E: int, n: int, seed: int = 0):
-    """Channel (b, e) pairs to check at full size: the corners, wave boundaries, random others."""
-    g = np.random.default_rng(seed)
-    picks = {(0, 0), (Bsz - 1, E - 1), (0, E - 1), (Bsz - 1, 0)}
-    for e in (63, 64, 65, E // 2):
-        if e < E:
-            picks.add((int(g.integers(Bsz)), e))
-    while len(picks) < n:
-        picks.add((int(g.integers(Bsz)), int(g.integers(E))))
-    return sorted(picks)
-
-
-def single_channel_inputs(params: dict, e: int, seq: dict) -> dict:
-    """A (1, L, 1) case for the oracle made of channel e's parameters and per-token sequences
-    x, z, dt_raw (L,) and B, C (L, N)."""
-    L = len(seq["x"])
-    return {
-        "x": np.asarray(seq["x"], np.float32).reshape(1, L, 1),
-        "z": np.asarray(seq["z"], np.float32).reshape(1, L, 1),
-        "dt_raw": np.asarray(seq["dt_raw"], np.float32).reshape(1, L, 1),
-        "B": np.asarray(seq["B"], np.float32).reshape(1, L, -1),
-        "C": np.asarray(seq["C"], np.float32).reshape(1, L, -1),
-        "A_log": params["A_log"][e:e + 1], "D": params["D"][e:e + 1],
-        "dt_bias": params["dt_bias"][e:e + 1], "conv_w": params["conv_w"][e:e + 1],
-        "conv_b": params["conv_b"][e:e + 1], "dt_min": params["dt_min"],
-        "dt_max": params["dt_max"],
-        **{k: params[k] for k in ("conv_activation", "discretization") if k in params},
-    }
 
 
 def make_case(B, L, E, act="f32", dt_mode="axon", seed=0, caches=False):

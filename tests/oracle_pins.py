@@ -643,6 +643,110 @@ def pin_ssd_continuation_and_empty(lib=None):
     np.testing.assert_array_equal(z["ssm_state"], np.zeros_like(h0))
 
 
+# ---- the term-magnitude output (a tolerance input of the stress parity cases) -------------------
+def _lti_states(Abar, Bbar, x):
+    """h_t,n = sum_{s<=t} Abar_n^(t-s) Bbar_n x_s (h_0 = 0), from a lower-triangular matrix of
+    powers per state: the LTI closed form of the state [GLOSS]."""
+    L = len(x)
+    lag = np.arange(L)[:, None] - np.arange(L)[None, :]
+    H = np.empty((L, len(Abar)))
+    for n in range(len(Abar)):
+        T = np.where(lag >= 0, np.power(Abar[n], np.maximum(lag, 0)), 0.0)
+        H[:, n] = T @ (Bbar[n] * x)
+    return H
+
+
+def pin_magnitude_closed_form(lib=None, L=48, seed=61):
+    """The oracle's ``mag`` output is |SiLU(z_t)| (sum_n |C_n h_t,n| + |D u_t|), the size of the
+    terms the gated output y_t = SiLU(z_t) (C . h_t + D u_t) sums [AXON "ZOH discretization",
+    "Gating"]. In the LTI case (constant B, C and dt, identity convolution, h_0 = 0) the states
+    are known in closed form, so every term is: the pin checks ``mag`` from the whole-tensor and
+    the per-channel entry points against that, with B, C and x of mixed signs so that a signed sum
+    differs from the sum of magnitudes."""
+    inp, _ = _case(L, seed=seed)
+    g = np.random.default_rng(seed + 100)
+    Bc = g.standard_normal(N).astype(np.float32)
+    Cc = g.standard_normal(N).astype(np.float32)
+    inp["B"][:] = Bc
+    inp["C"][:] = Cc
+    inp["conv_w"][:] = np.array([0, 0, 0, 1], np.float32)
+    inp["conv_b"][:] = 0
+    delta = 0.125
+    inp["dt_min"] = inp["dt_max"] = delta
+    A = -np.exp(inp["A_log"][0].astype(np.float64))
+    x = inp["x"][0, :, 0].astype(np.float64)
+    H = _lti_states(np.exp(delta * A), delta * Bc.astype(np.float64), x)
+    gate = np.abs(_silu(inp["z"][0, :, 0]))
+    expect = gate * (np.abs(H * Cc.astype(np.float64)[None, :]).sum(axis=1)
+                     + np.abs(float(inp["D"][0]) * x))
+    r = oracle.prefill(inp, lib=lib, magnitude=True)
+    np.testing.assert_allclose(r["mag"][0, :, 0], expect, rtol=1e-11, atol=1e-13)
+    c = oracle.channel(inp, 0, 0, lib=lib)
+    np.testing.assert_allclose(c["mag"], expect, rtol=1e-11, atol=1e-13)
+    # signed and absolute sums must differ on this case, or the pin could not tell them apart
+    signed = gate * np.abs((H * Cc.astype(np.float64)[None, :]).sum(axis=1)
+                           + float(inp["D"][0]) * x)
+    assert np.max(np.abs(signed - expect) / expect) > 0.1
+
+
+def pin_ssd_magnitude(lib=None):
+    """The SSD core's ``mag`` output is sum_n |C_t,n h_t[p, n]| + |D x_t,p| [WIKI "Mamba-2
+    block"]; the states h_t come from the masked-matrix (duality) form in closed form,
+    h_t = sum_{s<=t} exp(cum_t - cum_s) dt_s x_s B_s^T + exp(cum_t) h0, evaluated with numpy."""
+    inp, h0 = _ssd_case(62, Bsz=1, L=19, H=2, P=3, Nn=5)
+    r = oracle.ssd_scan(inp, state_in=h0, lib=lib, magnitude=True)
+    _, L, H, P = inp["x"].shape
+    dt = _ssd_dt(inp)
+    A = -np.exp(inp["A_log"].astype(np.float64))
+    Bm = inp["B"][0].astype(np.float64)
+    Cm = inp["C"][0].astype(np.float64)
+    for hd in range(H):
+        cum = np.cumsum(dt[0, :, hd] * A[hd])
+        X = inp["x"][0, :, hd].astype(np.float64)
+        for t in range(L):
+            w = np.exp(cum[t] - cum[:t + 1]) * dt[0, :t + 1, hd]
+            ht = (w[:, None] * X[:t + 1]).T @ Bm[:t + 1] + np.exp(cum[t]) * h0[0, hd]  # (P, N)
+            expect = np.abs(ht * Cm[t][None, :]).sum(axis=1) + np.abs(inp["D"][hd] * X[t])
+            np.testing.assert_allclose(r["mag"][0, t, hd], expect, rtol=1e-10, atol=1e-12)
+
+
+# ---- bfloat16 storage of intermediates (the layer oracle's rounding) ---------------------------
+# (value, its bfloat16 rounding to nearest with ties to even): bf16 keeps 8 significant bits,
+# so near 1 its spacing is 2^-7; 1 + 2^-8 and 1 + 3 * 2^-8 are the ties between neighbours with
+# an even and an odd last bit.
+BF16_TABLE = [
+    (1.0, 1.0), (-1.0, -1.0), (0.0, 0.0),
+    (1.0 + 2.0 ** -8, 1.0),                       # tie, lower neighbour even
+    (1.0 + 3 * 2.0 ** -8, 1.0 + 2 * 2.0 ** -7),   # tie, upper neighbour even
+    (-(1.0 + 3 * 2.0 ** -8), -(1.0 + 2 * 2.0 ** -7)),
+    (1.0 + 2.0 ** -8 + 2.0 ** -20, 1.0 + 2.0 ** -7),   # just above a tie: rounds up
+    (1.0 + 2.0 ** -8 - 2.0 ** -20, 1.0),               # just below: rounds down
+    (3.0, 3.0), (2.0 ** -130, 2.0 ** -130),       # exact (a subnormal of float32 included)
+    (1000.5, 1000.0), (1001.0, 1000.0), (1003.0, 1004.0),  # spacing 8 between 512 and 1024
+]
+
+
+def pin_store_as_bf16(store=None):
+    """``store_as(a, "bf16")`` rounds to the nearest bfloat16 with ties to even, as the GPU path
+    stores bf16 intermediates [R10: y and layer intermediates in the activation dtype]: exact
+    values of a table of ties and near-ties, and agreement with torch's CPU bfloat16 conversion
+    (a library routine) on random float32 values; ``store_as(a, "f32")`` is the float32
+    rounding."""
+    import torch
+
+    store = store or oracle.store_as
+    vals = np.array([v for v, _ in BF16_TABLE], np.float64)
+    want = np.array([w for _, w in BF16_TABLE], np.float64)
+    got = np.asarray(store(vals, "bf16"), np.float64)
+    np.testing.assert_array_equal(got, want)
+    g = np.random.default_rng(63)
+    r = (g.standard_normal(4096) * np.exp2(g.integers(-20, 20, 4096))).astype(np.float32)
+    lib_round = torch.from_numpy(r).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(np.asarray(store(r, "bf16"), np.float32), lib_round)
+    np.testing.assert_array_equal(np.asarray(store(r.astype(np.float64) * (1 + 1e-9), "f32")),
+                                  (r.astype(np.float64) * (1 + 1e-9)).astype(np.float32))
+
+
 ALL_PINS = [
     pin_ssd_masked_matrix_form, pin_ssd_reduces_to_axon, pin_ssd_continuation_and_empty,
     pin_layer_reduces_to_path, pin_layer_projections, pin_layer_step_equals_prefill,
@@ -651,4 +755,5 @@ ALL_PINS = [
     pin_lti_closed_form, pin_glossary_worked_example, pin_zero_input_decay, pin_dt_clip_bounds,
     pin_softplus_values, pin_A_from_A_log, pin_conv_shift, pin_conv_correlation,
     pin_brute_force, pin_decode_equals_prefill, pin_prefill_continuation, pin_empty_sequence,
+    pin_magnitude_closed_form, pin_ssd_magnitude,
 ]

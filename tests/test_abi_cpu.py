@@ -228,6 +228,50 @@ def test_layer_forward_rejects_bad_arguments():
     assert _lforward() == A.AXON_ERR_INVALID_ARGUMENT                 # context without a handle
 
 
+def _lcheck(shape=None, params=None, ws_bytes=1 << 32, weights=None, **over):
+    """axon_layer_forward_check on host addresses spread far apart (compared, never read)."""
+    b = _buffers()
+    b.update(over)
+    w = weights or A.LayerWeights(b.get("W_in", P + (5 << 30)), b.get("W_f", P + (6 << 30)),
+                                  b.get("W_out", P + (7 << 30)), params or _params())
+    return A.raw_layer_forward_check(shape or _lshape(), w, b["x"], b["cin"], b["sin"], b["y"],
+                                     b["cout"], b["sout"], b["ws"], ws_bytes)
+
+
+def test_layer_check_accepts_valid_arguments():
+    assert _lcheck() == A.AXON_OK
+    b = _buffers()
+    assert _lcheck(cout=b["cin"], sout=b["sin"]) == A.AXON_OK    # in-place caches
+    assert _lcheck(cin=None, sin=None) == A.AXON_OK               # zero initial caches
+    assert _lforward() == A.AXON_ERR_INVALID_ARGUMENT              # a context without a handle
+
+
+@pytest.mark.parametrize("case", [
+    "out_over_x", "out_over_W_in", "out_over_W_f", "out_over_W_out", "out_over_A_log",
+    "out_over_conv_w", "out_over_cache_in", "out_over_state_in", "out_over_cache_out",
+    "out_over_state_out", "out_over_ws", "ws_over_x", "ws_over_W_f", "ws_over_cache_in",
+    "ws_over_state_out", "ws_over_D", "cache_out_over_x", "cache_out_over_W_out",
+    "cache_out_over_dt_bias", "cache_out_partly_over_cache_in", "cache_out_over_state_in",
+    "cache_out_over_state_out", "state_out_over_x", "state_out_over_W_in",
+    "state_out_over_conv_b", "state_out_partly_over_state_in", "state_out_over_cache_in"])
+def test_layer_check_rejects_forbidden_aliasing(case):
+    b = _buffers()
+    prm = _params()
+    win, wf, wout = P + (5 << 30), P + (6 << 30), P + (7 << 30)
+    target, what = case.split("_over_") if "_partly_over_" not in case else \
+        (case.split("_partly_over_")[0], case.split("_partly_over_")[1])
+    addr = {"x": b["x"], "W_in": win, "W_f": wf, "W_out": wout, "A_log": prm.A_log,
+            "D": prm.D, "dt_bias": prm.dt_bias, "conv_w": prm.conv_w, "conv_b": prm.conv_b,
+            "cache_in": b["cin"], "state_in": b["sin"], "cache_out": b["cout"],
+            "state_out": b["sout"], "ws": b["ws"]}[what]
+    if "_partly_over_" in case:
+        addr += 16  # a partial overlap: exact equality is the allowed in-place form
+    key = {"out": "y", "ws": "ws", "cache_out": "cout", "state_out": "sout"}[target]
+    assert _lcheck(**{key: addr}) == A.AXON_ERR_INVALID_ARGUMENT, case
+    # the forward call rejects it the same way, before looking at the context
+    assert _lforward(**{key: addr}) == A.AXON_ERR_INVALID_ARGUMENT, case
+
+
 # ---- Mamba-2 SSD core ----------------------------------------------------------------------------
 def _ssd_shape(batch=1, seqlen=200, heads=4, bf16=False, head_dim=64, d_state=128):
     return A.make_ssd_shape(batch, seqlen, heads, bf16, head_dim=head_dim, d_state=d_state)

@@ -5,6 +5,8 @@ order; for that reason the conv cache (which holds x-branch projection outputs) 
 a tolerance here, not bit for bit: 1e-5 relative in fp32, one bf16 ulp (2^-8) in bf16."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 
@@ -60,7 +62,7 @@ def _ref(inp, act, caches=None, variant=None):
     return oracle.layer_forward(inp["x_in"], inp["W_in"], inp["W_f"], inp["W_out"], prm,
                                 conv_cache_in=None if caches is None else caches[0],
                                 ssm_state_in=None if caches is None else caches[1], act=act,
-                                threads=8)
+                                threads=max(1, min(16, os.cpu_count() or 1)))
 
 
 def _compare(out, cache, state, ref, act, what):
@@ -133,6 +135,7 @@ def test_layer_steps_equal_prefill(layer):
     assert_close(host(cache), host(c_full), CACHE_TOL["f32"], "cache")
 
 
+@pytest.mark.timeout(600)
 def test_layer_full_axon_shape(layer):
     """The Axon-SSM layer configuration: D = 2560, E = 7680, N = 16, K = 4 over 2048 tokens,
     fp32, whole output against the oracle."""
@@ -144,3 +147,17 @@ def test_layer_full_axon_shape(layer):
     say("[layer] full Axon shape: oracle")
     ref = _ref(inp, "f32")
     _compare(out, cache, state, ref, "f32", "layer full Axon shape")
+
+
+@pytest.mark.timeout(900)
+def test_layer_full_batch8_bf16(layer):
+    """The benchmarked bf16 layer: 8 x 4096 tokens, D = 2560, E = 7680, whole output, state and
+    cache against the oracle (its projections in float64, intermediates stored as bf16)."""
+    w = workloads.workload(2)
+    say("[layer] bf16 8 x 4096, D 2560: drawing inputs")
+    inp = workloads.layer_inputs(w, 2560)
+    say("[layer] bf16 8 x 4096, D 2560: GPU")
+    out, cache, state = _run(layer, inp, "bf16")
+    say("[layer] bf16 8 x 4096, D 2560: oracle")
+    ref = _ref(inp, "bf16")
+    _compare(out, cache, state, ref, "bf16", "layer bf16 batch 8")

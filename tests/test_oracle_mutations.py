@@ -5,6 +5,7 @@ import os
 import subprocess
 import tempfile
 
+import numpy as np
 import pytest
 
 import oracle
@@ -60,6 +61,20 @@ MUTATIONS = {
     "ssd_state_in_ignored": ("h[i] = j->state_in ? j->state_in[bh * P * N + i] : 0.0;",
                              "h[i] = 0.0;"),
     "state_in_ignored": ("h[n] = h_in ? h_in[n] : 0.0;", "h[n] = 0.0;"),
+    "mag_signed_sum": ("mag += fabs((double)Cm[t * bc_stride + n] * h[n]);",
+                       "mag += (double)Cm[t * bc_stride + n] * h[n];"),
+    "mag_drops_skip": ("mag += fabs(D * u);", ""),
+    "mag_without_gate": ("mag_out[t * y_stride] = mag * fabs(gate);",
+                         "mag_out[t * y_stride] = mag;"),
+    "mag_before_update": (
+        "      acc += (double)Cm[t * bc_stride + n] * h[n];\n"
+        "      mag += fabs((double)Cm[t * bc_stride + n] * h[n]);",
+        "      acc += (double)Cm[t * bc_stride + n] * h[n];\n"
+        "      mag += fabs((double)Cm[t * bc_stride + n] * (h[n] - bbar * u));"),
+    "ssd_mag_signed_sum": ("size += fabs((double)Ct[n] * h[p * N + n]);",
+                           "size += (double)Ct[n] * h[p * N + n];"),
+    "ssd_mag_drops_skip": ("if (mt) mt[p] = size + fabs((double)j->D[hd] * (double)xt[p]);",
+                           "if (mt) mt[p] = size;"),
 }
 
 
@@ -74,6 +89,37 @@ def _build_variant(name, old, new, tmpdir):
     subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-I", inc,
                     "-o", path_so, path_c, "-lm", "-lpthread"], check=True)
     return oracle.load_library(path_so)
+
+
+# Planted mistakes in the bfloat16 rounding of ``oracle.store_as`` (Python): truncation, ties away
+# from zero, and rounding to 7 instead of 8 significant bits.
+def _bf16_truncate(a, act):
+    a32 = np.ascontiguousarray(np.asarray(a, np.float64).astype(np.float32))
+    return (a32.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32) if act == "bf16" else a32
+
+
+def _bf16_ties_away(a, act):
+    a32 = np.ascontiguousarray(np.asarray(a, np.float64).astype(np.float32))
+    u = (a32.view(np.uint32) + np.uint32(0x8000)) & np.uint32(0xFFFF0000)
+    return u.view(np.float32) if act == "bf16" else a32
+
+
+def _bf16_short_mantissa(a, act):
+    a32 = np.ascontiguousarray(np.asarray(a, np.float64).astype(np.float32))
+    u = a32.view(np.uint32)
+    u = (u + np.uint32(0xFFFF) + ((u >> np.uint32(17)) & np.uint32(1))) & np.uint32(0xFFFE0000)
+    return u.view(np.float32) if act == "bf16" else a32
+
+
+@pytest.mark.parametrize("store", [_bf16_truncate, _bf16_ties_away, _bf16_short_mantissa],
+                         ids=lambda f: f.__name__)
+def test_planted_bf16_rounding_mistake_is_caught(store):
+    with pytest.raises(AssertionError):
+        oracle_pins.pin_store_as_bf16(store=store)
+
+
+def test_store_as_pin_passes():
+    oracle_pins.pin_store_as_bf16()
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
