@@ -73,6 +73,8 @@ typedef enum {
 } axon_status;
 
 typedef enum { AXON_F32 = 0, AXON_BF16 = 1 } axon_dtype;
+/* Enumerated fields of the structs below are int32_t holding these values, so that any integer a
+ * caller stores is a defined value that the checks can reject. */
 
 typedef struct {
   int64_t batch;      /* B */
@@ -80,7 +82,7 @@ typedef struct {
   int64_t d_inner;    /* E, channels */
   int64_t d_state;    /* N, must be 16 */
   int64_t d_conv;     /* K, must be 4 */
-  axon_dtype act_dtype;
+  int32_t act_dtype;  /* an axon_dtype value */
 } axon_ssm_shape;
 
 typedef struct {
@@ -109,8 +111,9 @@ enum { AXON_DISC_FIRST_ORDER = 0, AXON_DISC_ZOH = 1 };
 /* Library version as 10000*major + 100*minor + patch. */
 int axon_version(void);
 
-/* Static description of a status code; never NULL. */
-const char* axon_status_string(axon_status status);
+/* Static description of a status code (any int; unknown codes give "unknown status"); never
+ * NULL. */
+const char* axon_status_string(int status);
 
 /* Bytes of device workspace axon_ssm_prefill needs for this shape (0 is possible). A pure
  * function of the shape: no device is queried. Returns 0 for an invalid shape as well, so call
@@ -177,7 +180,8 @@ typedef struct {
   int64_t d_inner;    /* E */
   int64_t d_state;    /* N, must be 16 */
   int64_t d_conv;     /* K, must be 4 */
-  axon_dtype act_dtype;  /* x_in, out, the three projection weights and the intermediates */
+  int32_t act_dtype;  /* an axon_dtype: x_in, out, the three projection weights and the
+                        * intermediates */
 } axon_layer_shape;
 
 typedef struct {
@@ -253,7 +257,7 @@ typedef struct {
   int64_t n_heads;   /* H */
   int64_t head_dim;  /* P, must be 64 */
   int64_t d_state;   /* N, must be 128 */
-  axon_dtype act_dtype;
+  int32_t act_dtype;  /* an axon_dtype value */
 } axon_ssd_shape;
 
 typedef struct {

@@ -92,8 +92,12 @@ def _load(lib=None):
         return lib
     with _lock:
         if _lib is None:
-            build(force=False)
-            _lib = load_library(_LIB_PATH)
+            override = os.environ.get("AXON_ORACLE_LIB")  # e.g. the sanitizer build
+            if override:
+                _lib = load_library(override)
+            else:
+                build(force=False)
+                _lib = load_library(_LIB_PATH)
         return _lib
 
 

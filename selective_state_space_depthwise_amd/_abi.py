@@ -12,7 +12,8 @@ import re
 import threading
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libaxonscan.so")
+# AXONSCAN_LIB selects another build of the library (the sanitizer build of build.py).
+LIB_PATH = os.environ.get("AXONSCAN_LIB") or os.path.join(PKG, "libaxonscan.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "axonscan.h")
 
 AXON_OK = 0

@@ -39,7 +39,9 @@ struct PrefillPlan {
 };
 
 // A pure function of the shape (no device query), so the workspace size is known up front.
-PrefillPlan plan_prefill(int64_t batch, int64_t seqlen, int64_t d_inner);
+// With a workspace limit, the plan takes fewer time chunks until its workspace fits.
+PrefillPlan plan_prefill(int64_t batch, int64_t seqlen, int64_t d_inner, size_t max_workspace);
+PrefillPlan plan_prefill_uncapped(int64_t batch, int64_t seqlen, int64_t d_inner);
 
 struct PrefillLaunch {
   int64_t batch, seqlen, d_inner;
@@ -84,6 +86,15 @@ inline bool overlaps(const Span& a, const Span& b) {
 void param_spans(const axon_ssm_params* p, int64_t E, Span out[5]);
 
 int launch_prefill(const PrefillLaunch& a, const PrefillPlan& plan, void* stream);
+// Every check of axon_ssm_prefill (shape, parameters, pointers, workspace size, aliasing) and
+// the launch description; nothing is launched. library_scratch: the workspace is the library's
+// own scratch array (not checked for null or overlap with the caller's buffers).
+axon_status prepare_prefill(const axon_ssm_shape* shape, const axon_ssm_params* params,
+                            const void* x, const void* z, const void* dt_raw, const void* B,
+                            const void* C, const float* conv_cache_in, const float* ssm_state_in,
+                            void* y, float* conv_cache_out, float* ssm_state_out,
+                            void* workspace, size_t workspace_bytes, bool library_scratch,
+                            size_t max_workspace, PrefillLaunch* launch, PrefillPlan* plan);
 // The C-ABI checks of a parameter block (pointers, alignment, clips, variants).
 axon_status validate_params(const axon_ssm_params* p);
 constexpr int64_t kMaxChannels = int64_t(1) << 23;  // d_inner limit of the prefill kernels

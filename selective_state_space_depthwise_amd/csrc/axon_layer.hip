@@ -278,7 +278,7 @@ LayerPlan plan_layer(const axon_layer_shape* s) {
   p.idw = take(E * kConv * sizeof(float));
   p.idb = take(E * sizeof(float));
   p.cache = take(static_cast<size_t>(s->batch) * kHalo * E * sizeof(float));
-  p.scan_plan = plan_prefill(s->batch, s->seqlen, s->d_inner);
+  p.scan_plan = plan_prefill(s->batch, s->seqlen, s->d_inner, SIZE_MAX);
   p.scan = take(p.scan_plan.workspace_bytes);
   p.gemm = take(kGemmWorkspace);
   p.total = off;

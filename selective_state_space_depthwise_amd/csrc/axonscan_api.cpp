@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 
 #include "axon_internal.h"
 
@@ -134,7 +135,22 @@ void set_chunks(PrefillPlan& plan, int64_t seqlen, int64_t M, int64_t step) {
 
 }  // namespace
 
-PrefillPlan plan_prefill(int64_t batch, int64_t seqlen, int64_t d_inner) {
+PrefillPlan plan_prefill(int64_t batch, int64_t seqlen, int64_t d_inner, size_t max_workspace) {
+  PrefillPlan plan = plan_prefill_uncapped(batch, seqlen, d_inner);
+  // Fewer chunks until the workspace fits (one chunk needs none).
+  const int step = plan.kernel == kChanScan ? 8 : (plan.row_waves == 4 ? 32 : 16);
+  for (int64_t M = plan.chunks - 1; plan.workspace_bytes > max_workspace && M >= 1; --M) {
+    PrefillPlan p = plan;
+    p.off_carry_h = p.off_carry_s = p.off_carry_in = p.off_halo = 0;
+    p.workspace_bytes = 0;
+    set_chunks(p, seqlen, M, step);
+    layout_workspace(p, batch * d_inner);
+    plan = p;
+  }
+  return plan;
+}
+
+PrefillPlan plan_prefill_uncapped(int64_t batch, int64_t seqlen, int64_t d_inner) {
   PrefillPlan plan;
   const int64_t channels = batch * d_inner;
   const bool chan = kPlanKernel == 1 || (kPlanKernel == 2 && channels < kSinglePassChannels);
@@ -168,32 +184,14 @@ PrefillPlan plan_prefill(int64_t batch, int64_t seqlen, int64_t d_inner) {
 
 }  // namespace axon
 
-extern "C" {
+namespace axon {
 
-int axon_version(void) { return kVersion; }
-
-const char* axon_status_string(axon_status status) {
-  switch (status) {
-    case AXON_OK: return "ok";
-    case AXON_ERR_INVALID_ARGUMENT: return "invalid argument";
-    case AXON_ERR_UNSUPPORTED: return "unsupported shape, dtype or variant";
-    case AXON_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
-    case AXON_ERR_HIP: return "HIP launch or runtime error";
-  }
-  return "unknown status";
-}
-
-size_t axon_ssm_prefill_workspace_bytes(const axon_ssm_shape* shape) {
-  if (check_shape(shape, true) != AXON_OK) return 0;
-  return axon::plan_prefill(shape->batch, shape->seqlen, shape->d_inner).workspace_bytes;
-}
-
-axon_status axon_ssm_prefill(const axon_ssm_shape* shape, const axon_ssm_params* params,
-                             const void* x, const void* z, const void* dt_raw, const void* B,
-                             const void* C, const float* conv_cache_in,
-                             const float* ssm_state_in, void* y, float* conv_cache_out,
-                             float* ssm_state_out, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+axon_status prepare_prefill(const axon_ssm_shape* shape, const axon_ssm_params* params,
+                            const void* x, const void* z, const void* dt_raw, const void* B,
+                            const void* C, const float* conv_cache_in, const float* ssm_state_in,
+                            void* y, float* conv_cache_out, float* ssm_state_out,
+                            void* workspace, size_t workspace_bytes, bool library_scratch,
+                            size_t max_workspace, PrefillLaunch* launch, PrefillPlan* plan_out) {
   axon_status st = check_shape(shape, true);
   if (st != AXON_OK) return st;
   st = check_params(params);
@@ -212,23 +210,26 @@ axon_status axon_ssm_prefill(const axon_ssm_shape* shape, const axon_ssm_params*
   if ((conv_cache_in && !aligned16(conv_cache_in)) || (ssm_state_in && !aligned16(ssm_state_in)))
     return AXON_ERR_INVALID_ARGUMENT;
 
-  const axon::PrefillPlan plan = axon::plan_prefill(Bsz, L, E);
+  const PrefillPlan plan = plan_prefill(Bsz, L, E, max_workspace);
   const bool needs_ws = L > 0 && plan.workspace_bytes > 0;
   if (needs_ws) {
     if (workspace_bytes < plan.workspace_bytes) return AXON_ERR_WORKSPACE_TOO_SMALL;
-    if (!workspace || !aligned16(workspace)) return AXON_ERR_INVALID_ARGUMENT;
+    if (!library_scratch && (!workspace || !aligned16(workspace)))
+      return AXON_ERR_INVALID_ARGUMENT;
   }
 
   const size_t act_bytes = elt * Bsz * L * E;
-  const size_t bc_bytes = elt * Bsz * L * axon::kState;
-  const size_t cache_bytes = sizeof(float) * Bsz * axon::kHalo * E;
-  const size_t state_bytes = sizeof(float) * Bsz * E * axon::kState;
+  const size_t bc_bytes = elt * Bsz * L * kState;
+  const size_t cache_bytes = sizeof(float) * Bsz * kHalo * E;
+  const size_t state_bytes = sizeof(float) * Bsz * E * kState;
   Span in_x = span(x, act_bytes), in_z = span(z, act_bytes), in_dt = span(dt_raw, act_bytes);
   Span in_b = span(B, bc_bytes), in_c = span(C, bc_bytes);
   Span in_cache = span(conv_cache_in, cache_bytes), in_state = span(ssm_state_in, state_bytes);
   Span out_y = span(y, act_bytes), out_cache = span(conv_cache_out, cache_bytes);
   Span out_state = span(ssm_state_out, state_bytes);
-  Span ws = needs_ws ? span(workspace, plan.workspace_bytes) : Span{};
+  // The library's own scratch is a separate allocation of the code object: no caller buffer
+  // can overlap it.
+  Span ws = needs_ws && !library_scratch ? span(workspace, plan.workspace_bytes) : Span{};
   Span prm[5];
   param_spans(params, E, prm);
 
@@ -254,7 +255,8 @@ axon_status axon_ssm_prefill(const axon_ssm_shape* shape, const axon_ssm_params*
   for (const Span& r : rw)
     if (overlaps(ws, r)) return AXON_ERR_INVALID_ARGUMENT;
 
-  axon::PrefillLaunch a{};
+  PrefillLaunch& a = *launch;
+  a = PrefillLaunch{};
   a.batch = Bsz;
   a.seqlen = L;
   a.d_inner = E;
@@ -279,6 +281,45 @@ axon_status axon_ssm_prefill(const axon_ssm_shape* shape, const axon_ssm_params*
   a.conv_cache_out = conv_cache_out;
   a.ssm_state_out = ssm_state_out;
   a.workspace = needs_ws ? workspace : nullptr;
+  *plan_out = plan;
+  return AXON_OK;
+}
+
+}  // namespace axon
+
+extern "C" {
+
+
+int axon_version(void) { return kVersion; }
+
+const char* axon_status_string(int status) {
+  switch (status) {
+    case AXON_OK: return "ok";
+    case AXON_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case AXON_ERR_UNSUPPORTED: return "unsupported shape, dtype or variant";
+    case AXON_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case AXON_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+size_t axon_ssm_prefill_workspace_bytes(const axon_ssm_shape* shape) {
+  if (check_shape(shape, true) != AXON_OK) return 0;
+  return axon::plan_prefill(shape->batch, shape->seqlen, shape->d_inner, SIZE_MAX).workspace_bytes;
+}
+
+axon_status axon_ssm_prefill(const axon_ssm_shape* shape, const axon_ssm_params* params,
+                             const void* x, const void* z, const void* dt_raw, const void* B,
+                             const void* C, const float* conv_cache_in,
+                             const float* ssm_state_in, void* y, float* conv_cache_out,
+                             float* ssm_state_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  axon::PrefillLaunch a;
+  axon::PrefillPlan plan;
+  const axon_status st = axon::prepare_prefill(
+      shape, params, x, z, dt_raw, B, C, conv_cache_in, ssm_state_in, y, conv_cache_out,
+      ssm_state_out, workspace, workspace_bytes, false, SIZE_MAX, &a, &plan);
+  if (st != AXON_OK) return st;
   return axon::launch_prefill(a, plan, stream) == 0 ? AXON_OK : AXON_ERR_HIP;
 }
 
