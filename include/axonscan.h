@@ -140,6 +140,21 @@ axon_status axon_ssm_prefill(const axon_ssm_shape* shape, const axon_ssm_params*
                              void* y, float* conv_cache_out, float* ssm_state_out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same prefill without allocating and without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). The time-chunked scan's workspace is a 64 MiB scratch array the library
+ * holds on each GPU it runs on until the process ends; for shapes whose chunked plan would need
+ * more, the plan takes fewer time chunks (same results to rounding, possibly slower), so every
+ * shape axon_ssm_prefill accepts is accepted. Arguments, checks and results otherwise as
+ * axon_ssm_prefill; the stream must belong to the current device. Calls on one GPU share its
+ * scratch: calls that overlap in time on the same GPU race (serialise them, e.g. on one
+ * stream). AXON_ERR_HIP if the scratch's device address cannot be obtained. */
+axon_status axon_ssm_prefill_noalloc(const axon_ssm_shape* shape, const axon_ssm_params* params,
+                                     const void* x, const void* z, const void* dt_raw,
+                                     const void* B, const void* C, const float* conv_cache_in,
+                                     const float* ssm_state_in, void* y, float* conv_cache_out,
+                                     float* ssm_state_out, void* stream);
+
 /* Decode step: one token per batch row, with the caches updated in place
  * [AXON "Autoregressive decoding": the cache pair carries the convolution padding and the
  * hidden state from one step to the next].

@@ -97,6 +97,9 @@ def load():
         lib.axon_ssm_prefill.argtypes = [
             ctypes.POINTER(Shape), ctypes.POINTER(Params), P, P, P, P, P, P, P, P, P, P, P,
             ctypes.c_size_t, P]
+        lib.axon_ssm_prefill_noalloc.restype = ctypes.c_int
+        lib.axon_ssm_prefill_noalloc.argtypes = [
+            ctypes.POINTER(Shape), ctypes.POINTER(Params), P, P, P, P, P, P, P, P, P, P, P]
         lib.axon_ssm_decode_step.restype = ctypes.c_int
         lib.axon_ssm_decode_step.argtypes = [
             ctypes.POINTER(Shape), ctypes.POINTER(Params), P, P, P, P, P, P, P, P, P]
@@ -155,6 +158,14 @@ def raw_prefill(shape: Shape, params: Params, x, z, dt_raw, B, C, cache_in, stat
     return load().axon_ssm_prefill(ctypes.byref(shape), ctypes.byref(params), x, z, dt_raw, B, C,
                                    cache_in, state_in, y, cache_out, state_out, workspace,
                                    int(workspace_bytes_), stream)
+
+
+def raw_prefill_noalloc(shape: Shape, params: Params, x, z, dt_raw, B, C, cache_in, state_in,
+                        y, cache_out, state_out, stream) -> int:
+    """axon_ssm_prefill_noalloc with integer pointers. Returns the status code."""
+    return load().axon_ssm_prefill_noalloc(ctypes.byref(shape), ctypes.byref(params), x, z,
+                                           dt_raw, B, C, cache_in, state_in, y, cache_out,
+                                           state_out, stream)
 
 
 def raw_decode_step(shape: Shape, params: Params, x, z, dt_raw, B, C, cache, state, y,

@@ -22,7 +22,7 @@ MICRO_SOURCE = "axon_microbench.hip"
 MICRO_LIB = os.path.join(PKG, "libaxonmicro.so")
 
 HIP_SOURCES = ["axon_kernels.hip", "axon_rowscan.hip", "axon_chanscan.hip", "axon_layer.hip",
-               "axon_ssd.hip"]
+               "axon_ssd.hip", "axon_noalloc.hip"]
 CXX_SOURCES = ["axonscan_api.cpp"]
 ARCH = "gfx950"
 ROCM_LIB = "/opt/rocm/lib"  # hipBLASLt (the layer's projection GEMMs)

@@ -337,3 +337,25 @@ def test_ssd_rejects_bad_arguments():
     assert _ssd(ws=b["B"]) == A.AXON_ERR_INVALID_ARGUMENT             # workspace overlaps B
     assert _ssd(sout=b["sin"] + 1024) == A.AXON_ERR_INVALID_ARGUMENT  # partial state overlap
     assert _ssd(sout=b["y"]) == A.AXON_ERR_INVALID_ARGUMENT          # state out overlaps y
+
+
+# ---- the allocation-free prefill: every check happens before any device call ----------------
+def _noalloc(shape=None, params=None, **over):
+    b = _buffers()
+    b.update(over)
+    return A.raw_prefill_noalloc(shape or _shape(), params or _params(), b["x"], b["z"], b["dt"],
+                                 b["B"], b["C"], b["cin"], b["sin"], b["y"], b["cout"], b["sout"],
+                                 None)
+
+
+def test_prefill_noalloc_rejects_bad_arguments():
+    assert _noalloc(shape=_shape(d_state=8)) == A.AXON_ERR_UNSUPPORTED
+    assert _noalloc(shape=_shape(batch=0)) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _noalloc(params=_params(dt_min=2.0, dt_max=1.0)) == A.AXON_ERR_INVALID_ARGUMENT
+    for name in ["x", "z", "dt", "B", "C", "y", "cout", "sout"]:
+        assert _noalloc(**{name: None}) == A.AXON_ERR_INVALID_ARGUMENT, name
+        assert _noalloc(**{name: _buffers()[name] + 4}) == A.AXON_ERR_INVALID_ARGUMENT, name
+    b = _buffers()
+    assert _noalloc(y=b["x"]) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _noalloc(cout=b["cin"] + 16) == A.AXON_ERR_INVALID_ARGUMENT
+    assert _noalloc(sout=b["cout"]) == A.AXON_ERR_INVALID_ARGUMENT
