@@ -561,9 +561,39 @@ def bench_micro():
             hbm[f"{name}_{blocks}_workgroups"] = {
                 "GB_per_s": round(moved / (out[0] / 1e3) / 1e9, 1), "ms": round(out[0], 4),
                 "bytes_moved": moved}
-    print(json.dumps({"micro": "gfx950 instruction issue and HBM streaming",
+    # The row scan's activation reads: lane rows of 16 lanes reading 64-, 128- or 256-byte
+    # segments of one token, 240 workgroups of 8 waves, 2048 x 7680 fp32 (and the same bytes
+    # at 2 and 4 x the channels).
+    for kind, seg in ((2, 64), (3, 128), (4, 256)):
+        nbytes = 2048 * 7680 * 4
+        rc = lib.axon_micro_hbm(kind, nbytes, 20, 1, out)
+        if rc:
+            raise RuntimeError(f"micro hbm segment {seg}: hip error {rc}")
+        hbm[f"row_pattern_read_{seg}B_segments"] = {
+            "GB_per_s": round(nbytes / (out[0] / 1e3) / 1e9, 1), "ms": round(out[0], 4),
+            "bytes_moved": nbytes}
+    # LDS: bytes delivered per CU clock (the measured clock) for each lane pattern.
+    lib.axon_micro_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.POINTER(ctypes.c_double)]
+    ghz = float(np.median(clock_ghz))
+    lds = {}
+    for kind, name, nbytes in ((0, "read_b128_distinct", 1024), (1, "read_b128_row_broadcast", 1024),
+                               (2, "read_b128_all_same", 1024), (3, "write_b128_distinct", 1024)):
+        lds[name] = {}
+        for wps in (1, 2, 4):
+            iters = 4000
+            rc = lib.axon_micro_lds(kind, wps, iters, out)
+            if rc:
+                raise RuntimeError(f"micro lds {name}: hip error {rc}")
+            instrs_per_cu = iters * 16 * 4 * wps
+            cycles = out[0] * 1e-3 * ghz * 1e9
+            lds[name][f"{wps}_wave_per_simd"] = {
+                "cu_cycles_per_instr": round(cycles / instrs_per_cu, 3),
+                "bytes_per_cu_cycle": round(nbytes * instrs_per_cu / cycles, 1),
+                "ms": round(out[0], 4)}
+    print(json.dumps({"micro": "gfx950 instruction issue, LDS and HBM streaming",
                       "s_memtime_clock_GHz": round(float(np.median(clock_ghz)), 4),
-                      "simds": simds, "alu": alu, "hbm": hbm}), flush=True)
+                      "simds": simds, "alu": alu, "lds": lds, "hbm": hbm}), flush=True)
 
 
 def _kernel_source_sha():
@@ -573,7 +603,7 @@ def _kernel_source_sha():
     csrc = os.path.join(ROOT, "selective_state_space_depthwise_amd", "csrc")
     # the sources the prefill kernels are built from
     for name in ("axon_device.h", "axon_internal.h", "axon_kernels.hip", "axon_rowscan.hip",
-                 "axonscan_api.cpp"):
+                 "axon_chanscan.hip", "axonscan_api.cpp"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]

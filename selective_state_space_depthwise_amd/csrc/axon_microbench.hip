@@ -9,6 +9,8 @@
 // least two VALU instructions earlier, so no wait states are needed beyond those written.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include <cstddef>
 #include <cstdint>
 
@@ -288,6 +290,69 @@ __global__ __launch_bounds__(256) void read_kernel(const float4* __restrict__ sr
   if (s == 12345.678f) sink[0] = s;  // keeps the loads; never true for the zero-filled input
 }
 
+// Reads a (T, E) fp32 matrix the way the row scan reads its activations: workgroups of 8 waves
+// over 2 x 16 lanes x VEC channels, each lane row of 16 lanes reading one token's 16 x VEC
+// contiguous channels (64, 128 or 256 bytes), two tokens per lane per 32-token tile, four tiles
+// of loads in flight. T is a multiple of 128 and E of 32 * VEC.
+template <int VEC>
+__global__ __launch_bounds__(512) void segment_read_kernel(const float* __restrict__ src,
+                                                           float* sink, int64_t T, int64_t E) {
+  using V = typename std::conditional<VEC == 1, float,
+            typename std::conditional<VEC == 2, float2, float4>::type>::type;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int grp = wid / 4, w = wid % 4, q = lane >> 4, c = lane & 15;
+  const int64_t ch = static_cast<int64_t>(blockIdx.x) * 32 * VEC + (grp * 16 + c) * VEC;
+  const int tau0 = (4 * w + q) * 2;
+  float s = 0.0f;
+  for (int64_t t = 0; t < T; t += 128) {
+    V v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t tok = t + (j / 2) * 32 + tau0 + (j % 2);
+      v[j] = *reinterpret_cast<const V*>(src + tok * E + ch);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float* f = reinterpret_cast<const float*>(&v[j]);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) s += f[i];
+    }
+  }
+  if (s == 12345.678f) sink[0] = s;  // keeps the loads; never true for the zero-filled input
+}
+
+// LDS read / write throughput of one wave pattern: 16 ds_read_b128 (or ds_write_b128) per loop
+// iteration per wave, lane addresses by kind: 0 every lane distinct (1 KB of distinct data per
+// instruction), 1 distinct within a 16-lane row and equal across the 4 rows (the row scan's
+// (dt, dt*u) reads), 2 every lane the same address, 3 ds_write_b128 with distinct lanes.
+// Addresses stay within the 16 KB buffer.
+constexpr int kLdsKinds = 4;
+template <int KIND>
+__global__ __launch_bounds__(256) void lds_kernel(int iters, float* sink) {
+  __shared__ float4 buf[1024];
+  const int lane = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < 1024; i += 256) buf[i] = make_float4(i, 1.0f, 2.0f, 3.0f);
+  __syncthreads();
+  const int idx = KIND == 1 ? (lane & 15) : KIND == 2 ? 0 : lane;
+  float acc = 0.0f;
+  for (int it = 0; it < iters; ++it) {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if constexpr (KIND == 3) {
+        buf[idx + j * 64] = make_float4(acc, acc, acc, acc);
+      } else {
+        const float4 v = buf[idx + j * 64];
+        acc += (v.x + v.y) + (v.z + v.w);
+      }
+    }
+    if constexpr (KIND == 3) acc += 1.0f;
+  }
+  __syncthreads();
+  if constexpr (KIND == 3) acc += buf[(threadIdx.x * 7) & 1023].y;
+  sink[static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x] = acc;
+}
+
 template <int K>
 hipError_t launch_alu(int wps, int iters, float* sink, unsigned long long* clocks,
                       hipStream_t s) {
@@ -367,11 +432,59 @@ int axon_micro_alu(int kind, int waves_per_simd, int iters, double* out) {
   return static_cast<int>(e);
 }
 
+// Runs LDS kind `kind` (lds_kernel) on 256 * waves_per_simd workgroups of 4 waves for `iters`
+// iterations after one untimed launch. out[0] = elapsed ms of the timed launch.
+int axon_micro_lds_kinds(void) { return kLdsKinds; }
+int axon_micro_lds(int kind, int waves_per_simd, int iters, double* out) {
+  if (kind < 0 || kind >= kLdsKinds || waves_per_simd < 1 || waves_per_simd > 8 || iters < 1 ||
+      !out)
+    return static_cast<int>(hipErrorInvalidValue);
+  float* sink = nullptr;
+  hipError_t e = hipMalloc(&sink, sizeof(float) * 256 * 256 * waves_per_simd);
+  if (e != hipSuccess) return static_cast<int>(e);
+  auto run = [&](int it) -> hipError_t {
+    const dim3 grid(256 * waves_per_simd), block(256);
+    switch (kind) {
+      case 0: hipLaunchKernelGGL(lds_kernel<0>, grid, block, 0, nullptr, it, sink); break;
+      case 1: hipLaunchKernelGGL(lds_kernel<1>, grid, block, 0, nullptr, it, sink); break;
+      case 2: hipLaunchKernelGGL(lds_kernel<2>, grid, block, 0, nullptr, it, sink); break;
+      default: hipLaunchKernelGGL(lds_kernel<3>, grid, block, 0, nullptr, it, sink); break;
+    }
+    return hipGetLastError();
+  };
+  hipEvent_t e0, e1;
+  (void)hipEventCreate(&e0);
+  (void)hipEventCreate(&e1);
+  e = run(iters);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) {
+    (void)hipEventRecord(e0, nullptr);
+    e = run(iters);
+    (void)hipEventRecord(e1, nullptr);
+  }
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.0f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  out[0] = ms;
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  (void)hipFree(sink);
+  return static_cast<int>(e);
+}
+
 // Streams `bytes` (a multiple of 16) through HBM `reps` times after one untimed pass:
 // kind 0 = copy (bytes read + bytes written per pass), kind 1 = read only. out[0] = mean ms per
 // pass. Workgroups: 256 threads, `blocks` of them (grid-stride loop).
+// Kinds 2, 3, 4: the row scan's access pattern (segment_read_kernel) with 64-, 128- and
+// 256-byte segments per lane row, over E = 7680 x (1, 2, 4) channels and T = bytes / (4 E) tokens
+// (bytes must make T a multiple of 128; `blocks` is unused: E / (32 x VEC) workgroups, 240).
 int axon_micro_hbm(int kind, size_t bytes, int reps, int blocks, double* out) {
-  if ((kind != 0 && kind != 1) || bytes == 0 || bytes % 16 || reps < 1 || blocks < 1 || !out)
+  if (kind < 0 || kind > 4 || bytes == 0 || bytes % 16 || reps < 1 || blocks < 1 || !out)
+    return static_cast<int>(hipErrorInvalidValue);
+  const int vec = kind == 2 ? 1 : kind == 3 ? 2 : 4;
+  const int64_t seg_e = int64_t(7680) * vec;
+  const int64_t seg_t = static_cast<int64_t>(bytes / 4) / seg_e;
+  if (kind >= 2 && (static_cast<size_t>(seg_t * seg_e * 4) != bytes || seg_t % 128 || seg_t < 128))
     return static_cast<int>(hipErrorInvalidValue);
   void *src = nullptr, *dst = nullptr;
   hipError_t e = hipMalloc(&src, bytes);
@@ -384,9 +497,19 @@ int axon_micro_hbm(int kind, size_t bytes, int reps, int blocks, double* out) {
   e = hipMemset(src, 0, bytes);
   const size_t n = bytes / 16;
   auto run = [&]() {
+    const unsigned seg_blocks = static_cast<unsigned>(seg_e / (32 * vec));
     if (kind == 0)
       hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(256), 0, nullptr,
                          static_cast<const float4*>(src), static_cast<float4*>(dst), n);
+    else if (kind == 2)
+      hipLaunchKernelGGL(segment_read_kernel<1>, dim3(seg_blocks), dim3(512), 0, nullptr,
+                         static_cast<const float*>(src), static_cast<float*>(dst), seg_t, seg_e);
+    else if (kind == 3)
+      hipLaunchKernelGGL(segment_read_kernel<2>, dim3(seg_blocks), dim3(512), 0, nullptr,
+                         static_cast<const float*>(src), static_cast<float*>(dst), seg_t, seg_e);
+    else if (kind == 4)
+      hipLaunchKernelGGL(segment_read_kernel<4>, dim3(seg_blocks), dim3(512), 0, nullptr,
+                         static_cast<const float*>(src), static_cast<float*>(dst), seg_t, seg_e);
     else
       hipLaunchKernelGGL(read_kernel, dim3(blocks), dim3(256), 0, nullptr,
                          static_cast<const float4*>(src), static_cast<float*>(dst), n);

@@ -468,11 +468,19 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
   // offsets; a tile that runs past the end of the sequence clamps its tokens to L - 1 through
   // its offsets. Both cases issue the same loads into the same registers with no per-lane
   // branch, so the compiler's wait counts stay exact.
+  // Per-tile addresses: the batch row's base plus one 64-bit product per tile (ts * E), shared
+  // by the three activation streams.
+  const Act* const xrow = xp + (b * L - 3) * E;
+  const Act* const drow = dtrp + b * L * E;
+  const Act* const zrow = zp + b * L * E;
+  Act* const yrow = yp + b * L * E;
+  const uint32_t tile_row = static_cast<uint32_t>(E * kElt);  // bytes per token of a stream
   auto load_seq = [&](int64_t ts, TileIn<TPL, NR>& in, const uint32_t (&xo)[TPL + 3],
                       const uint32_t (&to)[TPL], const uint32_t (&bo)[NR]) {
-    const rsrc_t rx = make_rsrc(xp + (b * L + ts - 3) * E);
-    const rsrc_t rd = make_rsrc(dtrp + (b * L + ts) * E);
-    const rsrc_t rz = make_rsrc(zp + (b * L + ts) * E);
+    const int64_t toff = ts * E;
+    const rsrc_t rx = make_rsrc(xrow + toff);
+    const rsrc_t rd = make_rsrc(drow + toff);
+    const rsrc_t rz = make_rsrc(zrow + toff);
     const rsrc_t rB = make_rsrc(Bp + ts * kState);
     const rsrc_t rC = make_rsrc(Cp + ts * kState);
 #pragma unroll
@@ -582,8 +590,7 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
       // of lanes past the last channel carry kNoStore, so the hardware drops them and no
       // branch is needed.
       const int64_t rem = te - ts < kTile ? te - ts : kTile;
-      const rsrc_t ry = make_rsrc_bounded(yp + (b * L + ts) * E,
-                                          static_cast<uint32_t>(rem * E * kElt));
+      const rsrc_t ry = make_rsrc_bounded(yrow + ts * E, static_cast<uint32_t>(rem) * tile_row);
 #pragma unroll
       for (int r = 0; r < TPL; ++r) {
         const int ix = ex_index(tau0 + r);

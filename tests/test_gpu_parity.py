@@ -35,21 +35,31 @@ def _gpu():
 
 
 SMALL = [
-    # (B, L, E, act, dt_mode, caches)
-    (1, 64, 32, "f32", "axon", False),      # the tiny workload itself
-    (1, 1000, 64, "f32", "axon", False),    # 3 time chunks, ragged last chunk
-    (3, 333, 100, "f32", "axon", True),     # ragged E and ragged last tile, caches in
-    (2, 517, 130, "bf16", "axon", True),    # 2 chunks
-    (1, 16384, 16, "f32", "axon", True),    # the maximum of 64 chunks
-    (1, 300, 7680, "f32", "axon", True),    # 2 states per lane (the Axon-SSM channel count)
-    (1, 200, 7700, "bf16", "axon", True),   # 2 states per lane, ragged channel groups
-    (2, 100, 9000, "f32", "axon", False),   # 4 states per lane
+    # (B, L, E, act, dt_mode, caches). Below 6144 channels (batch x d_inner) the lane-per-channel
+    # scan runs in time chunks; from there the row scan runs in one pass, 32-token tiles with one
+    # state per lane up to 16384 channels, 16-token tiles with two states per lane above.
+    (1, 64, 32, "f32", "axon", False),      # the tiny workload itself: one chunk
+    (1, 1000, 64, "f32", "axon", False),    # 14 chunks of 72 tokens, ragged last chunk
+    (3, 333, 100, "f32", "axon", True),     # 5 chunks, ragged E, caches in
+    (2, 517, 130, "bf16", "axon", True),    # 8 chunks, last one 13 tokens
+    (1, 16384, 16, "f32", "axon", True),    # the maximum of 256 chunks
     (2, 700, 48, "bf16", "wide", False),    # dt spanning [1e-4, 1] with +-50 clip hits
     (2, 700, 48, "f32", "wide", True),
     (1, 1, 70, "f32", "axon", True),        # L < K-1: the new cache mixes old cache and x
     (1, 2, 70, "bf16", "axon", True),
     (2, 3, 40, "f32", "axon", True),
-    (4, 96, 200, "f32", "axon", False),     # single chunk, several waves per row
+    (4, 96, 200, "f32", "axon", False),     # one chunk, 800 channels
+    (1, 300, 7680, "f32", "axon", True),    # row scan, one state per lane: 10 tiles, ragged
+    (1, 200, 7700, "bf16", "axon", True),   # ragged channel groups, 7 tiles
+    (2, 100, 9000, "f32", "axon", False),   # two states per lane: 7 tiles of 16
+    (1, 1, 7680, "f32", "axon", True),      # row scan, one token: the cache mixes old and new
+    (1, 3, 6200, "bf16", "axon", True),
+    (1, 32, 7680, "f32", "axon", True),     # exactly one tile
+    (1, 33, 7680, "f32", "axon", False),    # two tiles, the second of one token
+    (1, 96, 6144, "f32", "axon", True),     # three tiles: no pass of the four-tile loop
+    (1, 128, 7680, "bf16", "axon", False),  # four tiles: one pass of the loop, no tail
+    (2, 65, 9000, "bf16", "axon", True),    # 16-token tiles, 5 tiles, the last of one token
+    (1, 260, 16384, "f32", "wide", True),   # 16-token tiles, clip hits, 17 tiles
 ]
 
 
