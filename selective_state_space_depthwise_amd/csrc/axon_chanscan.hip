@@ -80,7 +80,7 @@ __device__ __forceinline__ void load8(const bf16_bits* p, float4& lo, float4& hi
 
 // Per-token values computed ahead of the state updates (for several tokens at once, so that
 // their dependent chains of conv, softplus and gate overlap): dt, dt*u (u itself for the exact
-// hold, which scales it per state), the gate SiLU(z) and the skip term D u SiLU(z).
+// hold, which scales it per state), the gate SiLU(z) and the skip term D u.
 struct Pre {
   float dt, du, g, q;
 };
@@ -96,7 +96,7 @@ __device__ __forceinline__ void prologue_token(float xm3, float xm2, float xm1, 
   p.du = kZoh ? u : p.dt * u;
   if constexpr (kFinal) {
     p.g = silu(zv);
-    p.q = Dv * u * p.g;
+    p.q = Dv * u;
   } else {
     S += p.dt;
   }
@@ -104,7 +104,8 @@ __device__ __forceinline__ void prologue_token(float xm3, float xm2, float xm1, 
 
 // The 16 state updates of one token: B row in registers (read ahead), C row read from its
 // staged copy at the start (final pass), used by the readout after the updates; returns the
-// gated output. The readout is summed in two halves to halve its dependent chain.
+// gated output. The readout is summed in two halves to halve its dependent chain, the skip term
+// starting the second.
 template <bool kFinal, bool kZoh>
 __device__ __forceinline__ float update_token(const Row& rb, const float4* crow, const Pre& p,
                                               const float (&rate)[kState],
@@ -133,13 +134,13 @@ __device__ __forceinline__ float update_token(const Row& rb, const float4* crow,
     }
   }
   if constexpr (kFinal) {
-    float a0 = rc.v[0] * h[0], a1 = rc.v[1] * h[1];
+    float a0 = rc.v[0] * h[0], a1 = fmaf(rc.v[1], h[1], p.q);
 #pragma unroll
     for (int n = 2; n < kState; n += 2) {
       a0 = fmaf(rc.v[n], h[n], a0);
       a1 = fmaf(rc.v[n + 1], h[n + 1], a1);
     }
-    return fmaf(a0 + a1, p.g, p.q);
+    return (a0 + a1) * p.g;
   } else {
     return 0.0f;
   }

@@ -37,11 +37,12 @@ __device__ __forceinline__ float load_uniform(const bf16_bits* p, int64_t i) {
 }
 
 __device__ __forceinline__ void store_act(float* p, int64_t i, float v) { p[i] = v; }
+// fp32 -> bf16 with round to nearest, ties to even: one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ bf16_bits f32_to_bf16(float v) {
+  return __builtin_bit_cast(bf16_bits, static_cast<__bf16>(v));
+}
 __device__ __forceinline__ void store_act(bf16_bits* p, int64_t i, float v) {
-  // round to nearest, ties to even
-  uint32_t u = __float_as_uint(v);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  p[i] = static_cast<bf16_bits>(u >> 16);
+  p[i] = f32_to_bf16(v);
 }
 
 // Raw buffer access: a wave-uniform 128-bit resource (base address in SGPRs) plus a 32-bit
@@ -92,9 +93,7 @@ __device__ __forceinline__ void store_buf_s<float>(rsrc_t r, uint32_t off, uint3
 template <>
 __device__ __forceinline__ void store_buf_s<bf16_bits>(rsrc_t r, uint32_t off, uint32_t soff,
                                                        float v) {
-  uint32_t u = __float_as_uint(v);  // round to nearest, ties to even
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(u >> 16), r, off, soff, 0);
+  __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, soff, 0);
 }
 
 template <typename Act>
@@ -105,9 +104,7 @@ __device__ __forceinline__ void store_buf<float>(rsrc_t r, uint32_t off, float v
 }
 template <>
 __device__ __forceinline__ void store_buf<bf16_bits>(rsrc_t r, uint32_t off, float v) {
-  uint32_t u = __float_as_uint(v);  // round to nearest, ties to even
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(u >> 16), r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
 }
 
 // A_n * log2(e) with A_n = -exp(A_log_n), so that exp(dt A_n) = exp2(dt * rate).

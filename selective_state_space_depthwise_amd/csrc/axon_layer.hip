@@ -66,11 +66,7 @@ __device__ __forceinline__ void store_vec(float* p, int64_t i, const float (&v)[
     for (int k = 0; k < V; ++k) p[i + k] = v[k];
   }
 }
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+__device__ __forceinline__ uint32_t bf16_rne(float f) { return f32_to_bf16(f); }
 template <int V>
 __device__ __forceinline__ void store_vec(bf16_bits* p, int64_t i, const float (&v)[V]) {
   if constexpr (V == 4) {
