@@ -67,12 +67,28 @@ def calibrate_copy(steps):
                       "bytes_written_per_dispatch": COPY_BYTES, "dispatches": steps}), flush=True)
 
 
-def cpu_baseline(inp, min_seconds=10.0):
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inp, min_seconds=10.0, single_seconds=3.0):
     """The oracle as it is (test infrastructure), timed on the host cores over whole passes of the
-    same workload until min_seconds have elapsed."""
+    same workload until min_seconds have elapsed, with as many threads as the process may use (at
+    most 16, a one-GPU share of the host); then single-threaded on each of the first two cores
+    the process may use, over the leading channels of the workload (the oracle's cost is linear
+    in channels), for about single_seconds each."""
     import oracle
 
-    threads = min(16, os.cpu_count() or 1)
+    avail = sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else []
+    nproc = len(avail) or (os.cpu_count() or 1)
+    threads = min(16, nproc)
     Bsz, L, E = inp["x"].shape
     oracle.prefill({k: (v[:, :8] if k in ("x", "z", "dt_raw", "B", "C") else v)
                     for k, v in inp.items()}, threads=threads)  # load / warm up
@@ -84,10 +100,44 @@ def cpu_baseline(inp, min_seconds=10.0):
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
-    return {"value": passes * Bsz * L / el, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"whole workload ({Bsz}x{L}x{E}), {passes} passes in {el:.1f} s, "
-                      f"{threads} threads over channels, double precision"}
+    out = {"value": passes * Bsz * L / el, "unit": "tokens/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"whole workload ({Bsz}x{L}x{E}), {passes} passes in {el:.1f} s, "
+                     f"{threads} threads over channels, double precision",
+           "nproc": nproc, "os_cpu_count": os.cpu_count(), "cpu_model": _cpu_model()}
+
+    # Single thread, pinned: time a slice of channels, grown until it takes single_seconds.
+    def channel_slice(ec):
+        d = dict(inp)
+        for k in ("x", "z", "dt_raw"):
+            d[k] = np.ascontiguousarray(inp[k][:, :, :ec])
+        for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b"):
+            d[k] = np.ascontiguousarray(inp[k][:ec])
+        return d
+
+    single = {}
+    cores = avail[:2] if len(avail) >= 2 else avail
+    if cores and hasattr(os, "sched_setaffinity"):
+        try:
+            for cpu in cores:
+                os.sched_setaffinity(0, {cpu})
+                ec = max(1, min(E, 8))
+                while True:
+                    d = channel_slice(ec)
+                    t0 = time.perf_counter()
+                    oracle.prefill(d, threads=1)
+                    el = time.perf_counter() - t0
+                    if el >= single_seconds or ec == E:
+                        break
+                    ec = min(E, max(ec * 2, int(ec * single_seconds / max(el, 1e-3))))
+                # tokens/s of the whole workload: the slice's rate scaled by its share of channels
+                single[f"c{cpu}"] = {"value": Bsz * L * (ec / E) / el, "unit": "tokens/s",
+                                     "sample": f"{Bsz}x{L}x{ec} (of {E} channels), {el:.2f} s, "
+                                               f"1 thread pinned to CPU {cpu}"}
+        finally:
+            os.sched_setaffinity(0, set(avail))
+    out["single_thread"] = single
+    return out
 
 
 def main():

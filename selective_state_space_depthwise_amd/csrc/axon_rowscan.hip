@@ -48,6 +48,7 @@ constexpr int tile_tokens() {
 
 struct RowArgs {
   int64_t B, L, E, T;
+  int xcd_remap;  // gridDim.x is a multiple of 8: keep neighbouring channel blocks on one XCD
   const void *x, *z, *dt_raw, *Bm, *Cm;
   const float *A_log, *D, *dt_bias, *conv_w, *conv_b;
   float dt_min, dt_max;
@@ -377,7 +378,14 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
   const int c = lane & 15;
   const int slot = grp * 16 + c;
   const int64_t b = blockIdx.y;
-  const int64_t e_raw = static_cast<int64_t>(blockIdx.x) * (kGroups * 16) + slot;
+  // Workgroups go to the eight XCDs round robin by linear id. When the channel blocks of a row
+  // are a multiple of 8 the XCD is blockIdx.x mod 8, and each XCD is given a contiguous range of
+  // channel blocks: the cache lines that two neighbouring blocks share (32 bf16 channels are half
+  // a 128-byte line) are then fetched into one L2 instead of two (8 x 4096 x 7680 bf16: L2
+  // fetches from 2.0x to 1.03x the bytes the scan reads).
+  const int64_t bx = a.xcd_remap ? (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8
+                                 : blockIdx.x;
+  const int64_t e_raw = bx * (kGroups * 16) + slot;
   const bool valid = e_raw < a.E;
   const int64_t e = valid ? e_raw : a.E - 1;
   const int g = w * 4 + q;  // this lane's state group: states g*SPL .. g*SPL + SPL - 1
@@ -651,6 +659,10 @@ int launch_row_scan_t(const PrefillLaunch& p, const PrefillPlan& plan, hipStream
   a.E = p.d_inner;
   a.T = plan.chunk_len;
   a.chunks = plan.chunks;
+  // Only where a workgroup's channels fill less than a 128-byte line (bf16): with fp32 the
+  // remap shares nothing and measured no gain.
+  a.xcd_remap = sizeof(Act) * kGroups * 16 < 128 &&
+                (p.d_inner + kGroups * 16 - 1) / (kGroups * 16) % 8 == 0 ? 1 : 0;
   a.x = p.x;
   a.z = p.z;
   a.dt_raw = p.dt_raw;
