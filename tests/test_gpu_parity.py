@@ -56,8 +56,15 @@ SMALL = [
     (1, 3, 6200, "bf16", "axon", True),
     (1, 32, 7680, "f32", "axon", True),     # exactly one tile
     (1, 33, 7680, "f32", "axon", False),    # two tiles, the second of one token
-    (1, 96, 6144, "f32", "axon", True),     # three tiles: no pass of the four-tile loop
-    (1, 128, 7680, "bf16", "axon", False),  # four tiles: one pass of the loop, no tail
+    (1, 96, 6144, "f32", "axon", True),     # three tiles: one pass of the three-tile loop
+    (1, 128, 7680, "bf16", "axon", False),  # four tiles: one loop pass and a tail of one
+    # Longer one-state-per-lane sequences: whole passes of the three-tile loop plus tails of
+    # one and two tiles, ragged last tiles.
+    (1, 256, 7680, "f32", "axon", True),    # 8 tiles: two loop passes, a tail of two
+    (1, 257, 6144, "bf16", "axon", True),   # 9 tiles, the last of one token, no tail
+    (1, 351, 7700, "f32", "axon", False),   # 11 tiles (a tail of two), ragged channel groups
+    (2, 290, 4000, "f32", "wide", True),    # 8000 channels in 2 rows, 10 tiles (a tail of one)
+    (1, 225, 6144, "bf16", "wide", False),  # 8 tiles, the last of one token, clip hits
     (2, 65, 9000, "bf16", "axon", True),    # 16-token tiles, 5 tiles, the last of one token
     (1, 260, 16384, "f32", "wide", True),   # 16-token tiles, clip hits, 17 tiles
 ]

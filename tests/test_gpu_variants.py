@@ -23,6 +23,7 @@ CASES = [
     # (B, L, E, act, dt_mode, caches)
     (1, 300, 7680, "f32", "axon", True),    # one state per lane, single pass
     (1, 200, 7700, "bf16", "axon", True),   # ragged channel groups
+    (1, 289, 6200, "bf16", "wide", True),   # 10 tiles, the last of one token, clip hits
     (2, 100, 9000, "f32", "axon", False),   # two states per lane, single pass
     (1, 1000, 64, "f32", "axon", False),    # time chunks
     (2, 700, 48, "f32", "wide", True),      # chunks, dt across [1e-4, 1] with clip hits
