@@ -560,13 +560,8 @@ MICRO_KINDS = ["fma", "exp", "dpp_row_newbcast_mul", "permlane32_swap", "state_u
                "exp_1_per_4_fma", "fma_plus_salu", "fma_dependent_chain", "exp_dependent_chain",
                "permlane16_swap", "exp_1_per_1_fma", "exp_1_per_2_fma", "exp_1_per_8_fma",
                "lane_per_channel_update", "lane_per_channel_update_exp_as_mul",
-               "16_exp_then_48_fma", "8_exp_then_24_fma_twice", "16_exp_then_48_fma_vop3"]
-# Per loop iteration: each wave of a role runs the body named (64 instructions unless stated).
-MICRO_PAIR_KINDS = ["both_64_fma", "both_64_exp", "64_exp_vs_64_fma",
-                    "8_decays_mul_exp_vs_8_updates_mul_fma_fmac",
-                    "both_8_state_updates_B_C_in_sgprs_80_instrs",
-                    "both_8_row_updates_without_exp_64_instrs",
-                    "both_8_state_updates_B_C_in_vgprs_80_instrs"]
+               "16_exp_then_48_fma", "8_exp_then_24_fma_twice", "16_exp_then_48_fma_vop3",
+               "fma_sgpr_operand"]
 
 
 def bench_micro():
@@ -647,21 +642,9 @@ def bench_micro():
                 "cu_cycles_per_instr": round(cycles / instrs_per_cu, 3),
                 "bytes_per_cu_cycle": round(nbytes * instrs_per_cu / cycles, 1),
                 "ms": round(out[0], 4)}
-    # Two waves per SIMD with different roles (pair_kernel): SIMD cycles per loop iteration, in
-    # which each of the two waves runs its role's body once.
-    lib.axon_micro_pair.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
-    pair = {}
-    for kind, name in enumerate(MICRO_PAIR_KINDS):
-        iters = 2000
-        rc = lib.axon_micro_pair(kind, iters, out)
-        if rc:
-            raise RuntimeError(f"micro pair {name}: hip error {rc}")
-        pair[name] = {"simd_cycles_per_iteration": round(out[0] * 1e-3 * ghz * 1e9 / iters, 1),
-                      "ms": round(out[0], 4)}
     print(json.dumps({"micro": "gfx950 instruction issue, LDS and HBM streaming",
                       "s_memtime_clock_GHz": round(float(np.median(clock_ghz)), 4),
-                      "simds": simds, "alu": alu, "lds": lds, "hbm": hbm, "pair": pair}),
-          flush=True)
+                      "simds": simds, "alu": alu, "lds": lds, "hbm": hbm}), flush=True)
 
 
 def _kernel_source_sha():

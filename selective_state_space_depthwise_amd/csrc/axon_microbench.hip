@@ -35,7 +35,8 @@ enum Kind : int {
   kBurst16 = 15,   // 16 v_exp_f32, then 48 v_fmac_f32 (the exps of a token grouped)
   kBurst8 = 16,    // 8 v_exp_f32, then 24 v_fmac_f32
   kBurst16v3 = 17, // 16 v_exp_f32, then 48 v_fma_f32 (VOP3)
-  kNumKinds = 18
+  kFmaSgpr = 18,   // 8 independent v_fmac_f32 chains with one operand in an SGPR
+  kNumKinds = 19
 };
 
 // VALU instructions per loop iteration of each kind (the SALU of kFmaSalu not counted).
@@ -45,7 +46,7 @@ __host__ __device__ constexpr int instrs_per_iter(int kind) {
        : kind == kFmaChain ? 32 : kind == kExpChain ? 32 : kind == kPerm16 ? 64
        : kind == kExpFma1 ? 64 : kind == kExpFma2 ? 72 : kind == kExpFma8 ? 72
        : kind == kChanUpd ? 80 : kind == kChanNoExp ? 80 : kind == kBurst16 ? 64
-       : kind == kBurst8 ? 64 : kind == kBurst16v3 ? 64 : 0;
+       : kind == kBurst8 ? 64 : kind == kBurst16v3 ? 64 : kind == kFmaSgpr ? 64 : 0;
 }
 
 #define F8(op) op(0) op(1) op(2) op(3) op(4) op(5) op(6) op(7)
@@ -89,6 +90,11 @@ __global__ __launch_bounds__(1024) void alu_kernel(int iters, float seed, float*
     if constexpr (kKind == kFma) {
       asm volatile(F8(FMA1) F8(FMA1) F8(FMA1) F8(FMA1) F8(FMA1) F8(FMA1) F8(FMA1) F8(FMA1)
                    : OUT8 : [m] "v"(m), [n] "v"(n));
+    } else if constexpr (kKind == kFmaSgpr) {
+#define FMAS1(i) "v_fmac_f32 %[a" #i "], %[s], %[n]\n\t"
+      asm volatile(F8(FMAS1) F8(FMAS1) F8(FMAS1) F8(FMAS1) F8(FMAS1) F8(FMAS1) F8(FMAS1)
+                   F8(FMAS1) : OUT8 : [s] "s"(seed), [n] "v"(n));
+#undef FMAS1
     } else if constexpr (kKind == kExp) {
       asm volatile(F8(EXP1) F8(EXP1) F8(EXP1) F8(EXP1) F8(EXP1) F8(EXP1) F8(EXP1) F8(EXP1)
                    : OUT8);
@@ -354,120 +360,6 @@ __global__ __launch_bounds__(256) void lds_kernel(int iters, float* sink) {
 }
 
 
-// Two roles on one SIMD: a workgroup of 8 waves puts waves w and w + 4 on the same SIMD, and
-// role = w / 4 picks what each runs, so each SIMD holds one wave of each role. Measures whether
-// work of one kind in one wave overlaps work of another kind in the other wave.
-enum PairKind : int {
-  kPairFma = 0,       // both roles: 8 independent v_fmac_f32 chains (64 per iteration)
-  kPairExp = 1,       // both roles: 64 v_exp_f32
-  kPairExpVsFma = 2,  // role 0: 64 v_exp_f32, role 1: 64 v_fmac_f32
-  kPairSplitUpd = 3,  // role 0: 8 x (v_mul, v_exp) decays; role 1: 8 x (v_mul, v_fma, v_fmac)
-  kPairSgprUpd = 4,   // both: the lane-per-channel update with B, C as SGPR operands (8 states)
-  kPairRowNoExp = 5,  // both: the row update without its exp (mul, dpp mul, fmac, dpp mul)
-  kPairChanUpd = 6,   // both: the lane-per-channel update with VGPR operands (8 states)
-  kPairKinds = 7
-};
-
-template <int kRole, int kKind>
-__device__ __forceinline__ void pair_body(float (&a)[8], float (&h)[8], float (&b)[8],
-                                          float (&nn)[8], float (&p)[8], float m, float n,
-                                          float sB, float sC) {
-  constexpr bool kDoFma = kKind == kPairFma || (kKind == kPairExpVsFma && kRole == 1);
-  constexpr bool kDoExp = kKind == kPairExp || (kKind == kPairExpVsFma && kRole == 0);
-  if constexpr (kDoFma) {
-    asm volatile(F8(FMA1) F8(FMA1) F8(FMA1) F8(FMA1) F8(FMA1) F8(FMA1) F8(FMA1) F8(FMA1)
-                 : OUT8 : [m] "v"(m), [n] "v"(n));
-  } else if constexpr (kDoExp) {
-    asm volatile(F8(EXP1) F8(EXP1) F8(EXP1) F8(EXP1) F8(EXP1) F8(EXP1) F8(EXP1) F8(EXP1)
-                 : OUT8);
-  } else if constexpr (kKind == kPairSplitUpd && kRole == 0) {
-#define SD_A(i) "v_mul_f32 %[a" #i "], %[m], %[n]\n\t"
-    asm volatile(F8(SD_A) F8(EXP1) : OUT8 : [m] "v"(m), [n] "v"(n));
-#undef SD_A
-  } else if constexpr (kKind == kPairSplitUpd && kRole == 1) {
-#define SU_B(i) "v_mul_f32 %[b" #i "], %[m], %[n]\n\t"
-#define SU_E(i) "v_fma_f32 %[h" #i "], %[a" #i "], %[h" #i "], %[b" #i "]\n\t"
-#define SU_R(i) "v_fmac_f32 %[p" #i "], %[m], %[h" #i "]\n\t"
-    asm volatile(F8(SU_B) F8(SU_E) F8(SU_R)
-                 : [b0] "+v"(b[0]), [b1] "+v"(b[1]), [b2] "+v"(b[2]), [b3] "+v"(b[3]),
-                   [b4] "+v"(b[4]), [b5] "+v"(b[5]), [b6] "+v"(b[6]), [b7] "+v"(b[7]),
-                   [h0] "+v"(h[0]), [h1] "+v"(h[1]), [h2] "+v"(h[2]), [h3] "+v"(h[3]),
-                   [h4] "+v"(h[4]), [h5] "+v"(h[5]), [h6] "+v"(h[6]), [h7] "+v"(h[7]),
-                   [p0] "+v"(p[0]), [p1] "+v"(p[1]), [p2] "+v"(p[2]), [p3] "+v"(p[3]),
-                   [p4] "+v"(p[4]), [p5] "+v"(p[5]), [p6] "+v"(p[6]), [p7] "+v"(p[7])
-                 : [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]),
-                   [a4] "v"(a[4]), [a5] "v"(a[5]), [a6] "v"(a[6]), [a7] "v"(a[7]), [m] "v"(m),
-                   [n] "v"(n));
-#undef SU_B
-#undef SU_E
-#undef SU_R
-  } else if constexpr (kKind == kPairSgprUpd || kKind == kPairChanUpd) {
-#define PU_A(i) "v_mul_f32 %[n" #i "], %[dt], %[r]\n\t"
-#define PU_D(i) "v_exp_f32 %[n" #i "], %[n" #i "]\n\t"
-#define PU_B(i) "v_mul_f32 %[b" #i "], %[RB], %[dtu]\n\t"
-#define PU_E(i) "v_fma_f32 %[h" #i "], %[n" #i "], %[h" #i "], %[b" #i "]\n\t"
-#define PU_R(i) "v_fmac_f32 %[p" #i "], %[RC], %[h" #i "]\n\t"
-#define PU_OUT                                                                               \
-  [n0] "+v"(nn[0]), [n1] "+v"(nn[1]), [n2] "+v"(nn[2]), [n3] "+v"(nn[3]), [n4] "+v"(nn[4]),  \
-      [n5] "+v"(nn[5]), [n6] "+v"(nn[6]), [n7] "+v"(nn[7]), [b0] "+v"(b[0]), [b1] "+v"(b[1]), \
-      [b2] "+v"(b[2]), [b3] "+v"(b[3]), [b4] "+v"(b[4]), [b5] "+v"(b[5]), [b6] "+v"(b[6]),    \
-      [b7] "+v"(b[7]), [p0] "+v"(p[0]), [p1] "+v"(p[1]), [p2] "+v"(p[2]), [p3] "+v"(p[3]),    \
-      [p4] "+v"(p[4]), [p5] "+v"(p[5]), [p6] "+v"(p[6]), [p7] "+v"(p[7]), [h0] "+v"(h[0]),    \
-      [h1] "+v"(h[1]), [h2] "+v"(h[2]), [h3] "+v"(h[3]), [h4] "+v"(h[4]), [h5] "+v"(h[5]),    \
-      [h6] "+v"(h[6]), [h7] "+v"(h[7])
-    if constexpr (kKind == kPairSgprUpd) {
-      asm volatile(F8(PU_A) F8(PU_D) F8(PU_B) F8(PU_E) F8(PU_R)
-                   : PU_OUT : [dt] "v"(m), [r] "v"(n), [RB] "s"(sB), [RC] "s"(sC), [dtu] "v"(a[2]));
-    } else {
-      asm volatile(F8(PU_A) F8(PU_D) F8(PU_B) F8(PU_E) F8(PU_R)
-                   : PU_OUT : [dt] "v"(m), [r] "v"(n), [RB] "v"(a[0]), [RC] "v"(a[1]),
-                     [dtu] "v"(a[2]));
-    }
-#undef PU_OUT
-#undef PU_A
-#undef PU_D
-#undef PU_B
-#undef PU_E
-#undef PU_R
-  } else {
-    asm volatile(F8(UPD_A) F8(UPD_B) F8(UPD_C) F8(UPD_E)
-                 : [n0] "+v"(nn[0]), [n1] "+v"(nn[1]), [n2] "+v"(nn[2]), [n3] "+v"(nn[3]),
-                   [n4] "+v"(nn[4]), [n5] "+v"(nn[5]), [n6] "+v"(nn[6]), [n7] "+v"(nn[7]),
-                   [b0] "+v"(b[0]), [b1] "+v"(b[1]), [b2] "+v"(b[2]), [b3] "+v"(b[3]),
-                   [b4] "+v"(b[4]), [b5] "+v"(b[5]), [b6] "+v"(b[6]), [b7] "+v"(b[7]),
-                   [p0] "+v"(p[0]), [p1] "+v"(p[1]), [p2] "+v"(p[2]), [p3] "+v"(p[3]),
-                   [p4] "+v"(p[4]), [p5] "+v"(p[5]), [p6] "+v"(p[6]), [p7] "+v"(p[7]),
-                   [h0] "+v"(h[0]), [h1] "+v"(h[1]), [h2] "+v"(h[2]), [h3] "+v"(h[3]),
-                   [h4] "+v"(h[4]), [h5] "+v"(h[5]), [h6] "+v"(h[6]), [h7] "+v"(h[7])
-                 : [dt] "v"(m), [r] "v"(n), [RB] "v"(a[0]), [RC] "v"(a[1]), [dtu] "v"(a[2]));
-  }
-}
-
-template <int kKind>
-__global__ __launch_bounds__(512) void pair_kernel(int iters, float seed, const float* sgpr_src,
-                                                   float* sink) {
-  float a[8], h[8], b[8], nn[8], p[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = seed * static_cast<float>(threadIdx.x + i);
-    h[i] = a[i];
-    b[i] = nn[i] = p[i] = 0.0f;
-  }
-  const float m = 0.999f + seed * 1e-6f, n = 1e-3f * seed;
-  const float sB = sgpr_src[0], sC = sgpr_src[1];  // wave-uniform: held in SGPRs
-  // Wave-uniform role (a scalar branch outside the loop, so no exec-mask handling inside it).
-  const int role1 = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 8));
-  if (role1) {
-    for (int it = 0; it < iters; ++it) pair_body<1, kKind>(a, h, b, nn, p, m, n, sB, sC);
-  } else {
-    for (int it = 0; it < iters; ++it) pair_body<0, kKind>(a, h, b, nn, p, m, n, sB, sC);
-  }
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s += a[i] + h[i] + p[i] + nn[i] + b[i];
-  sink[static_cast<size_t>(blockIdx.x) * 512 + threadIdx.x] = s;
-}
-
 // Workgroup size of the ALU kinds (threads); the grid keeps 256 * 4 * wps waves in total.
 int g_alu_wg_threads = 256;
 
@@ -536,6 +428,7 @@ int axon_micro_alu(int kind, int waves_per_simd, int iters, double* out) {
       case kBurst16: return launch_alu<kBurst16>(waves_per_simd, it, sink, clocks, nullptr);
       case kBurst8: return launch_alu<kBurst8>(waves_per_simd, it, sink, clocks, nullptr);
       case kBurst16v3: return launch_alu<kBurst16v3>(waves_per_simd, it, sink, clocks, nullptr);
+      case kFmaSgpr: return launch_alu<kFmaSgpr>(waves_per_simd, it, sink, clocks, nullptr);
       default: return launch_alu<kPerm16>(waves_per_simd, it, sink, clocks, nullptr);
     }
   };
@@ -665,52 +558,5 @@ int axon_micro_hbm(int kind, size_t bytes, int reps, int blocks, double* out) {
   return static_cast<int>(e);
 }
 
-
-// Runs pair kind `kind` (pair_kernel) on 256 workgroups of 8 waves (two waves per SIMD, one of
-// each role) for `iters` iterations after one untimed launch. out[0] = elapsed ms of the timed
-// launch. Returns 0 or a hipError_t value.
-int axon_micro_pair_kinds(void) { return kPairKinds; }
-int axon_micro_pair(int kind, int iters, double* out) {
-  if (kind < 0 || kind >= kPairKinds || iters < 1 || !out)
-    return static_cast<int>(hipErrorInvalidValue);
-  float* sink = nullptr;
-  float* src = nullptr;
-  hipError_t e = hipMalloc(&sink, sizeof(float) * 256 * 512);
-  if (e != hipSuccess) return static_cast<int>(e);
-  e = hipMalloc(&src, 2 * sizeof(float));
-  if (e == hipSuccess) e = hipMemset(src, 0, 2 * sizeof(float));
-  auto run = [&](int it) -> hipError_t {
-    const dim3 grid(256), block(512);
-    switch (kind) {
-      case kPairFma: hipLaunchKernelGGL(pair_kernel<kPairFma>, grid, block, 0, nullptr, it, 1.0f, src, sink); break;
-      case kPairExp: hipLaunchKernelGGL(pair_kernel<kPairExp>, grid, block, 0, nullptr, it, 1.0f, src, sink); break;
-      case kPairExpVsFma: hipLaunchKernelGGL(pair_kernel<kPairExpVsFma>, grid, block, 0, nullptr, it, 1.0f, src, sink); break;
-      case kPairSplitUpd: hipLaunchKernelGGL(pair_kernel<kPairSplitUpd>, grid, block, 0, nullptr, it, 1.0f, src, sink); break;
-      case kPairSgprUpd: hipLaunchKernelGGL(pair_kernel<kPairSgprUpd>, grid, block, 0, nullptr, it, 1.0f, src, sink); break;
-      case kPairRowNoExp: hipLaunchKernelGGL(pair_kernel<kPairRowNoExp>, grid, block, 0, nullptr, it, 1.0f, src, sink); break;
-      default: hipLaunchKernelGGL(pair_kernel<kPairChanUpd>, grid, block, 0, nullptr, it, 1.0f, src, sink); break;
-    }
-    return hipGetLastError();
-  };
-  hipEvent_t e0, e1;
-  (void)hipEventCreate(&e0);
-  (void)hipEventCreate(&e1);
-  if (e == hipSuccess) e = run(iters);
-  if (e == hipSuccess) e = hipDeviceSynchronize();
-  if (e == hipSuccess) {
-    (void)hipEventRecord(e0, nullptr);
-    e = run(iters);
-    (void)hipEventRecord(e1, nullptr);
-  }
-  if (e == hipSuccess) e = hipEventSynchronize(e1);
-  float ms = 0.0f;
-  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
-  out[0] = ms;
-  (void)hipEventDestroy(e0);
-  (void)hipEventDestroy(e1);
-  (void)hipFree(sink);
-  (void)hipFree(src);
-  return static_cast<int>(e);
-}
 
 }  // extern "C"
