@@ -528,7 +528,8 @@ def bench_ssd(args, w):
         "event_ms": {"mean": round(launch_ms, 5), "min": round(float(ev_ms.min()), 5),
                      "median": round(float(np.median(ev_ms)), 5)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": 157.3,
-                     "unit": "TFLOP/s", "frac": round(tflops / 157.3, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(tflops / 157.3, 4),
+                     "traffic": _measured_traffic(args.traffic_json, w.name, _ssd_source_sha()),
                      "flops_per_launch": flops,
                      "note": "fp32 matrix-core flops of the chunked form over the whole call "
                              "(four kernels)"},
@@ -645,6 +646,29 @@ def bench_micro():
     print(json.dumps({"micro": "gfx950 instruction issue, LDS and HBM streaming",
                       "s_memtime_clock_GHz": round(float(np.median(clock_ghz)), 4),
                       "simds": simds, "alu": alu, "lds": lds, "hbm": hbm}), flush=True)
+
+
+def _measured_traffic(path, name, sha):
+    """HBM bytes per call measured by rocprofv3 counters (profiles/traffic.json), if they were
+    taken on the current kernel sources; else None."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        entry = json.load(f).get(name)
+    if entry and entry.get("kernel_source_sha") == sha:
+        return entry.get("bytes_per_launch")
+    return None
+
+
+def _ssd_source_sha():
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "selective_state_space_depthwise_amd", "csrc")
+    for name in ("axon_device.h", "axon_ssd.hip"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
 
 
 def _kernel_source_sha():
