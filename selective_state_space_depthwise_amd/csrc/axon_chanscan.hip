@@ -266,11 +266,13 @@ __global__ __launch_bounds__(kChanBlock) __attribute__((amdgpu_waves_per_eu(kFin
   // state updates one token at a time. Each activation slot is reloaded with the next step's
   // token as soon as its prologue has consumed it (loads run kUnroll tokens ahead). The
   // scheduling barriers keep each token's LDS reads and stores in its own region.
-  float nx[kUnroll], nd[kUnroll], nz[kUnroll];
+  // The slots hold the raw loaded bits (bf16 is widened where the prologue reads it): a widening
+  // next to the load would sit inside the load's scheduling region and wait for its data.
+  uint32_t nx[kUnroll], nd[kUnroll], nz[kUnroll];
   auto slot_load = [&](rsrc_t rx, rsrc_t rd, rsrc_t rz, int j) {
-    nx[j] = load_buf_s<Act>(rx, voff, j * tok_bytes);
-    nd[j] = load_buf_s<Act>(rd, voff, j * tok_bytes);
-    if constexpr (kFinal) nz[j] = load_buf_s<Act>(rz, voff, j * tok_bytes);
+    nx[j] = load_raw_s<Act>(rx, voff, j * tok_bytes);
+    nd[j] = load_raw_s<Act>(rd, voff, j * tok_bytes);
+    if constexpr (kFinal) nz[j] = load_raw_s<Act>(rz, voff, j * tok_bytes);
   };
   if (kUnroll <= nt) {
     const rsrc_t rx = make_rsrc(xrow + tb * E), rd = make_rsrc(drow + tb * E);
@@ -296,12 +298,14 @@ __global__ __launch_bounds__(kChanBlock) __attribute__((amdgpu_waves_per_eu(kFin
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = 4 * half + i;
-          prologue_token<kFinal, kSilu, kZoh>(xm3, xm2, xm1, nx[j], nd[j],
-                                              kFinal ? nz[j] : 0.0f, cw.x, cw.y, cw.z, cw.w, cb,
+          const float x0 = raw_to_f32<Act>(nx[j]);
+          prologue_token<kFinal, kSilu, kZoh>(xm3, xm2, xm1, x0, raw_to_f32<Act>(nd[j]),
+                                              kFinal ? raw_to_f32<Act>(nz[j]) : 0.0f, cw.x, cw.y,
+                                              cw.z, cw.w, cb,
                                               dtb, Dv, a.dt_min, a.dt_max, pre[i], S);
           xm3 = xm2;
           xm2 = xm1;
-          xm1 = nx[j];
+          xm1 = x0;
           slot_load(rx, rd, rz, j);
         }
         __builtin_amdgcn_sched_barrier(0);

@@ -84,6 +84,29 @@ __device__ __forceinline__ float load_buf_s<bf16_bits>(rsrc_t r, uint32_t off, u
   return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0));
 }
 
+// The loaded bits without widening (fp32: the float's bits; bf16: the 16 bits zero-extended),
+// and their value: callers that prefetch keep the raw bits until use.
+template <typename Act>
+__device__ __forceinline__ uint32_t load_raw_s(rsrc_t r, uint32_t off, uint32_t soff);
+template <>
+__device__ __forceinline__ uint32_t load_raw_s<float>(rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+}
+template <>
+__device__ __forceinline__ uint32_t load_raw_s<bf16_bits>(rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
+}
+template <typename Act>
+__device__ __forceinline__ float raw_to_f32(uint32_t v);
+template <>
+__device__ __forceinline__ float raw_to_f32<float>(uint32_t v) {
+  return __uint_as_float(v);
+}
+template <>
+__device__ __forceinline__ float raw_to_f32<bf16_bits>(uint32_t v) {
+  return __uint_as_float(v << 16);
+}
+
 template <typename Act>
 __device__ __forceinline__ void store_buf_s(rsrc_t r, uint32_t off, uint32_t soff, float v);
 template <>

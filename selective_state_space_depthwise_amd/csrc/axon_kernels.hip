@@ -13,7 +13,8 @@ namespace {
 // Carry combine of the time-chunked prefill: one thread per (b, e, n) walks the M chunks in
 // order, H_0 = state_in, H_{c+1} = exp(A S_c) H_c + h_c, where S_c is the chunk's sum of dt
 // (the product of the chunk's decays exp(dt A)) and h_c its local final state from zero. The
-// carries of eight chunks are loaded before they are folded, so the loads of a group overlap.
+// carries are read in groups of eight chunks, the next group's loads issued before the current
+// group is folded, so one memory latency covers sixteen steps of the recurrence.
 constexpr int kCombineGroup = 8;
 
 __global__ __launch_bounds__(256) void carry_combine_kernel(int64_t B, int64_t E, int64_t M,
@@ -31,15 +32,17 @@ __global__ __launch_bounds__(256) void carry_combine_kernel(int64_t B, int64_t E
   const float rate = decay_rate_log2(A_log[e * kState + n]);
   float H = state_in ? state_in[idx] : 0.0f;
   carry_in[idx] = H;
-  // chunks 0..M-2 carry into 1..M-1
-  for (int64_t c0 = 0; c0 + 1 < M; c0 += kCombineGroup) {
-    float hc[kCombineGroup], sc[kCombineGroup];
+  // Chunks 0..M-2 carry into 1..M-1. Loads past the last carry re-read carry M-2 (never folded).
+  auto load_group = [&](int64_t c0, float (&hc)[kCombineGroup], float (&sc)[kCombineGroup]) {
 #pragma unroll
     for (int i = 0; i < kCombineGroup; ++i) {
       const int64_t c = c0 + i < M - 1 ? c0 + i : M - 2;
       hc[i] = carry_h[c * total + idx];
       sc[i] = carry_s[c * B * E + be];
     }
+  };
+  auto fold_group = [&](int64_t c0, const float (&hc)[kCombineGroup],
+                        const float (&sc)[kCombineGroup]) {
 #pragma unroll
     for (int i = 0; i < kCombineGroup; ++i) {
       if (c0 + i + 1 < M) {
@@ -47,6 +50,15 @@ __global__ __launch_bounds__(256) void carry_combine_kernel(int64_t B, int64_t E
         carry_in[(c0 + i + 1) * total + idx] = H;
       }
     }
+  };
+  if (M < 2) return;
+  float ha[kCombineGroup], sa[kCombineGroup], hb[kCombineGroup], sb[kCombineGroup];
+  load_group(0, ha, sa);
+  for (int64_t c0 = 0; c0 + 1 < M; c0 += 2 * kCombineGroup) {
+    load_group(c0 + kCombineGroup, hb, sb);
+    fold_group(c0, ha, sa);
+    load_group(c0 + 2 * kCombineGroup, ha, sa);
+    fold_group(c0 + kCombineGroup, hb, sb);
   }
 }
 
