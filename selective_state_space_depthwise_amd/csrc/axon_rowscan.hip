@@ -84,11 +84,18 @@ struct RowArgs {
 #define AXON_B1 AXON_BC(b0, RB, dtu, k0)
 #define AXON_B2 AXON_BC(b0, RB, dtu, k0) AXON_BC(b1, RB, dtu, k1)
 #define AXON_B4 AXON_BC(b0, RB, dtu, k0) AXON_BC(b1, RB, dtu, k1) AXON_BC(b2, RB, dtu, k2) AXON_BC(b3, RB, dtu, k3)
+// Readout products of the previous token, summed in the lane: C multiplies the first state of
+// each pair, CF adds the second with a DPP fmac after the block's state fmacs (so the fmac's
+// accumulator is two instructions old). SPL = 4 keeps two partial sums (states 0 + 1, 2 + 3).
+#define AXON_BCF(dst, src, mul, k)                                                            \
+  "v_fmac_f32_dpp %[" #dst "], %[" #src "], %[" #mul "] row_newbcast:%[" #k                  \
+  "] row_mask:0xf bank_mask:0xf\n\t"
 #define AXON_C1 AXON_BC(p0, RCp, h0, kp0)
-#define AXON_C2 AXON_BC(p0, RCp, h0, kp0) AXON_BC(p1, RCp, h1, kp1)
-#define AXON_C4                                                                           \
-  AXON_BC(p0, RCp, h0, kp0) AXON_BC(p1, RCp, h1, kp1) AXON_BC(p2, RCp, h2, kp2)             \
-  AXON_BC(p3, RCp, h3, kp3)
+#define AXON_C2 AXON_BC(p0, RCp, h0, kp0)
+#define AXON_C4 AXON_BC(p0, RCp, h0, kp0) AXON_BC(p1, RCp, h2, kp2)
+#define AXON_CF1
+#define AXON_CF2 AXON_BCF(p0, RCp, h1, kp1)
+#define AXON_CF4 AXON_BCF(p0, RCp, h1, kp1) AXON_BCF(p1, RCp, h3, kp3)
 #define AXON_E1S AXON_E1(0)
 #define AXON_E2S AXON_E1(0) AXON_E1(1)
 #define AXON_E4S AXON_E1(0) AXON_E1(1) AXON_E1(2) AXON_E1(3)
@@ -100,8 +107,8 @@ struct RowArgs {
 #define AXON_OUTN2 , [n0] "=&v"(an[0]), [n1] "=&v"(an[1])
 #define AXON_OUTN4 , [n0] "=&v"(an[0]), [n1] "=&v"(an[1]), [n2] "=&v"(an[2]), [n3] "=&v"(an[3])
 #define AXON_OUTP1 , [p0] "=&v"(pp[0])
-#define AXON_OUTP2 , [p0] "=&v"(pp[0]), [p1] "=&v"(pp[1])
-#define AXON_OUTP4 , [p0] "=&v"(pp[0]), [p1] "=&v"(pp[1]), [p2] "=&v"(pp[2]), [p3] "=&v"(pp[3])
+#define AXON_OUTP2 , [p0] "=&v"(pp[0])
+#define AXON_OUTP4 , [p0] "=&v"(pp[0]), [p1] "=&v"(pp[1])
 #define AXON_IN_COMMON [dtn] "v"(dtn), [dtu] "v"(dtu), [RB] "v"(RB), [RCp] "v"(RCp)
 #define AXON_IN1 , [r0] "v"(r[0]), [a0] "v"(ac[0]), [h0] "v"(h[0]), [k0] "i"(K), [kp0] "i"(KP)
 #define AXON_IN2                                                                          \
@@ -123,12 +130,12 @@ __device__ __forceinline__ void step(float dtn, float dtu, const float (&r)[SPL]
   float b[SPL];
 #define AXON_STEP(N)                                                                            \
   if constexpr (kNext && kPrev)                                                                 \
-    asm(AXON_AD##N AXON_B##N AXON_C##N AXON_E##N##S                                             \
+    asm(AXON_AD##N AXON_B##N AXON_C##N AXON_E##N##S AXON_CF##N                                  \
         : AXON_OUTB##N AXON_OUTN##N AXON_OUTP##N : AXON_IN_COMMON AXON_IN##N);                  \
   else if constexpr (kNext)                                                                     \
     asm(AXON_AD##N AXON_B##N AXON_E##N##S : AXON_OUTB##N AXON_OUTN##N : AXON_IN_COMMON AXON_IN##N); \
   else if constexpr (kPrev)                                                                     \
-    asm("s_nop 1\n\t" AXON_B##N AXON_C##N AXON_E##N##S                                          \
+    asm("s_nop 1\n\t" AXON_B##N AXON_C##N AXON_E##N##S AXON_CF##N                               \
         : AXON_OUTB##N AXON_OUTP##N : AXON_IN_COMMON AXON_IN##N);                               \
   else                                                                                          \
     asm("s_nop 1\n\t" AXON_B##N AXON_E##N##S : AXON_OUTB##N : AXON_IN_COMMON AXON_IN##N);
@@ -165,15 +172,22 @@ __device__ __forceinline__ void flush(float RCp, const float (&h)[SPL], float (&
     asm("s_nop 1\n\t" AXON_C1 "s_nop 1"
         : [p0] "=&v"(pp[0]) : [RCp] "v"(RCp), [h0] "v"(h[0]), [kp0] "i"(KP));
   } else if constexpr (SPL == 2) {
-    asm("s_nop 1\n\t" AXON_C2 "s_nop 1"
-        : [p0] "=&v"(pp[0]), [p1] "=&v"(pp[1])
+    asm("s_nop 1\n\t" AXON_C2 "s_nop 0\n\t" AXON_CF2 "s_nop 1"
+        : [p0] "=&v"(pp[0])
         : [RCp] "v"(RCp), [h0] "v"(h[0]), [h1] "v"(h[1]), [kp0] "i"(KP), [kp1] "i"(KP + 1));
   } else {
-    asm("s_nop 1\n\t" AXON_C4 "s_nop 1"
-        : [p0] "=&v"(pp[0]), [p1] "=&v"(pp[1]), [p2] "=&v"(pp[2]), [p3] "=&v"(pp[3])
+    asm("s_nop 1\n\t" AXON_C4 AXON_CF4 "s_nop 1"
+        : [p0] "=&v"(pp[0]), [p1] "=&v"(pp[1])
         : [RCp] "v"(RCp), [h0] "v"(h[0]), [h1] "v"(h[1]), [h2] "v"(h[2]), [h3] "v"(h[3]),
           [kp0] "i"(KP), [kp1] "i"(KP + 1), [kp2] "i"(KP + 2), [kp3] "i"(KP + 3));
   }
+}
+
+// The lane's readout of one token from the block's (or flush's) pre-summed products.
+template <int SPL>
+__device__ __forceinline__ float readout_sum(const float (&pp)[SPL]) {
+  if constexpr (SPL == 4) return pp[0] + pp[1];
+  return pp[0];
 }
 
 template <int SPL>
@@ -213,14 +227,14 @@ __device__ __forceinline__ void scan_tile_from(const float4 (&dd)[kTile / 2],
   constexpr bool kPrev = !kCarry && TAU >= 1;
   constexpr bool kNext = TAU + 1 < kTile;
   step<SPL, K, KP, kPrev, kNext>(dtn, dtu, rate, ac, RB[J], RC[JP], h, an, pp);
-  if constexpr (kPrev) P[TAU - 1] = lane_sum<SPL>(pp);
+  if constexpr (kPrev) P[TAU - 1] = readout_sum<SPL>(pp);
   if constexpr (kNext) {
 #pragma unroll
     for (int i = 0; i < SPL; ++i) ac[i] = an[i];
     scan_tile_from<SPL, kCarry, TAU + 1, kTile>(dd, rate, RB, RC, h, ac, P, S);
   } else if constexpr (!kCarry) {
     flush<SPL, ((kTile - 1) % TPR) * SPL>(RC[kTile * SPL / 16 - 1], h, pp);
-    P[kTile - 1] = lane_sum<SPL>(pp);
+    P[kTile - 1] = readout_sum<SPL>(pp);
   }
 }
 
@@ -322,7 +336,7 @@ __device__ __forceinline__ void scan_tile_zoh_from(
     scan_tile_zoh_from<SPL, kCarry, TAU + 1, kTile>(dd, rate, ia, zc, RB, RC, h, ac, yc, P, S);
   } else if constexpr (!kCarry) {
     flush<SPL, ((kTile - 1) % TPR) * SPL>(RC[kTile * SPL / 16 - 1], h, pp);
-    P[kTile - 1] = lane_sum<SPL>(pp);
+    P[kTile - 1] = readout_sum<SPL>(pp);
   }
 }
 
