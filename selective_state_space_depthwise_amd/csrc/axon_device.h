@@ -26,6 +26,20 @@ __device__ __forceinline__ float load_act(const float* p, int64_t i) { return p[
 __device__ __forceinline__ float load_act(const bf16_bits* p, int64_t i) {
   return bf16_to_f32(p[i]);
 }
+// Registers that hold an element's bits as loaded (fp32: 32 bits; bf16: 16 bits, so the
+// compiler never masks them), widened to fp32 by raw_to_f32 at use.
+template <typename Act>
+struct RawOf {
+  using type = uint32_t;
+};
+template <>
+struct RawOf<bf16_bits> {
+  using type = uint16_t;
+};
+__device__ __forceinline__ uint32_t load_act_raw(const float* p, int64_t i) {
+  return __float_as_uint(p[i]);
+}
+__device__ __forceinline__ uint16_t load_act_raw(const bf16_bits* p, int64_t i) { return p[i]; }
 
 // Wave-uniform reads of data no kernel writes (B_t / C_t rows): through the constant address
 // space, so the compiler issues scalar loads and the values arrive in SGPRs.
@@ -106,6 +120,22 @@ template <>
 __device__ __forceinline__ float raw_to_f32<bf16_bits>(uint32_t v) {
   return __uint_as_float(v << 16);
 }
+// The 16-bit form (RawOf<bf16_bits>): the shift drops whatever the register's upper half holds.
+__device__ __forceinline__ float raw16_to_f32(uint16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+template <typename Act>
+__device__ __forceinline__ typename RawOf<Act>::type load_raw_t(rsrc_t r, uint32_t off);
+template <>
+__device__ __forceinline__ uint32_t load_raw_t<float>(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+template <>
+__device__ __forceinline__ uint16_t load_raw_t<bf16_bits>(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ float widen(uint32_t v) { return __uint_as_float(v); }
+__device__ __forceinline__ float widen(uint16_t v) { return raw16_to_f32(v); }
 
 template <typename Act>
 __device__ __forceinline__ void store_buf_s(rsrc_t r, uint32_t off, uint32_t soff, float v);

@@ -355,13 +355,15 @@ __device__ __forceinline__ float rows_reduce4(float p0, float p1, float p2, floa
 
 // Inputs of one tile for this lane, loaded ahead of use. The lane's prologue / epilogue tokens
 // are TPL consecutive ones, tau0 .. tau0 + TPL - 1 with tau0 = (4 w + q) TPL, so its conv window
-// is TPL + 3 inputs. B / C registers are laid out as scan_tile_from reads them.
-template <int TPL, int NR>
+// is TPL + 3 inputs. B / C registers are laid out as scan_tile_from reads them. The registers
+// hold the loaded bits (bf16: zero-extended), widened to fp32 only where they are used, so a
+// load in flight is never copied or waited for before its use.
+template <int TPL, int NR, typename Raw>
 struct TileIn {
-  float xw[TPL + 3];  // x at tau0 - 3 .. tau0 + TPL - 1
-  float dr[TPL];
-  float zz[TPL];
-  float RB[NR], RC[NR];
+  Raw xw[TPL + 3];  // x at tau0 - 3 .. tau0 + TPL - 1 (tile 0: unused, see x0)
+  Raw dr[TPL];
+  Raw zz[TPL];
+  Raw RB[NR], RC[NR];
 };
 
 // kSilu: SiLU on the convolution output (Mamba-block variant); kZoh: exact zero-order hold.
@@ -461,34 +463,44 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
     }
   }
 
+  using Tile = TileIn<TPL, NR, typename RawOf<Act>::type>;
   auto load_x = [&](int64_t tt) -> float {
     if (tt < 0) return a.win_src ? a.win_src[(b * kHalo + (tt + kHalo)) * E + e] : 0.0f;
     return load_act(xp, (b * L + (tt < L ? tt : L - 1)) * E + e);
   };
   // The first two tiles: conv halo from the incoming window, tokens past the end clamped.
-  auto load_tile_first = [&](int64_t ts, TileIn<TPL, NR>& in) {
+  // The first two tiles: tokens past the end clamped. Tile 0's conv window may reach into the
+  // incoming window (fp32), so its x is read as values by the caller (x0); tile 1 starts at
+  // kTile > 3 tokens past the chunk start, so its window lies in x.
+  auto load_tile_first = [&](int64_t ts, Tile& in, bool with_x) {
     const int64_t t0 = ts + tau0;
+    if (with_x) {
 #pragma unroll
-    for (int j = 0; j < TPL + 3; ++j) in.xw[j] = load_x(t0 - 3 + j);
+      for (int j = 0; j < TPL + 3; ++j) {
+        const int64_t tt = t0 - 3 + j;
+        in.xw[j] = load_act_raw(xp, (b * L + (tt < L ? tt : L - 1)) * E + e);
+      }
+    }
 #pragma unroll
     for (int r = 0; r < TPL; ++r) {
       const int64_t tt = t0 + r < L ? t0 + r : L - 1;
-      in.dr[r] = load_act(dtrp, (b * L + tt) * E + e);
-      if constexpr (!kCarry) in.zz[r] = load_act(zp, (b * L + tt) * E + e);
+      in.dr[r] = load_act_raw(dtrp, (b * L + tt) * E + e);
+      if constexpr (!kCarry) in.zz[r] = load_act_raw(zp, (b * L + tt) * E + e);
     }
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
       int64_t tt = ts + j * TPR + c / SPL;
       tt = tt < L ? tt : L - 1;
       const int n = g * SPL + (c % SPL);
-      in.RB[j] = load_act(Bp, tt * kState + n);
-      if constexpr (!kCarry) in.RC[j] = load_act(Cp, tt * kState + n);
+      in.RB[j] = load_act_raw(Bp, tt * kState + n);
+      if constexpr (!kCarry) in.RC[j] = load_act_raw(Cp, tt * kState + n);
     }
   };
   // Tiles loaded inside the loop start at ts >= tb + 2 kTile >= 3, so their conv halo is in x,
-  // and at ts <= L - 1. Addresses are a wave-uniform buffer resource per tile plus 32-bit lane
-  // offsets; a tile that runs past the end of the sequence clamps its tokens to L - 1 through
-  // its offsets. Both cases issue the same loads into the same registers with no per-lane
+  // and at ts <= L - 1. Addresses are a wave-uniform buffer resource per tile plus fixed 32-bit
+  // lane offsets. Each resource's range ends at the end of the batch row's sequence, so in a
+  // tile that runs past it the hardware returns 0 for the missing tokens (they get dt = 0 and
+  // no store); every tile issues the same loads into the same registers with no per-lane
   // branch, so the compiler's wait counts stay exact.
   // Per-tile addresses: the batch row's base plus one 64-bit product per tile (ts * E), shared
   // by the three activation streams.
@@ -497,59 +509,45 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
   const Act* const zrow = zp + b * L * E;
   Act* const yrow = yp + b * L * E;
   const uint32_t tile_row = static_cast<uint32_t>(E * kElt);  // bytes per token of a stream
-  auto load_seq = [&](int64_t ts, TileIn<TPL, NR>& in, const uint32_t (&xo)[TPL + 3],
-                      const uint32_t (&to)[TPL], const uint32_t (&bo)[NR]) {
+  auto range = [](int64_t tokens, int64_t token_bytes) -> uint32_t {
+    const int64_t bytes = tokens * token_bytes;
+    return bytes < 0xffffffffLL ? static_cast<uint32_t>(bytes) : 0xffffffffu;
+  };
+  auto load_tile = [&](int64_t ts, Tile& in) {
     const int64_t toff = ts * E;
-    const rsrc_t rx = make_rsrc(xrow + toff);
-    const rsrc_t rd = make_rsrc(drow + toff);
-    const rsrc_t rz = make_rsrc(zrow + toff);
-    const rsrc_t rB = make_rsrc(Bp + ts * kState);
-    const rsrc_t rC = make_rsrc(Cp + ts * kState);
+    const int64_t left = L - ts;  // tokens from the tile's first to the end of the sequence
+    const rsrc_t rx = make_rsrc_bounded(const_cast<Act*>(xrow + toff), range(left + 3, tile_row));
+    const rsrc_t rd = make_rsrc_bounded(const_cast<Act*>(drow + toff), range(left, tile_row));
+    const rsrc_t rz = make_rsrc_bounded(const_cast<Act*>(zrow + toff), range(left, tile_row));
+    const rsrc_t rB =
+        make_rsrc_bounded(const_cast<Act*>(Bp + ts * kState), range(left, kState * kElt));
+    const rsrc_t rC =
+        make_rsrc_bounded(const_cast<Act*>(Cp + ts * kState), range(left, kState * kElt));
 #pragma unroll
-    for (int j = 0; j < TPL + 3; ++j) in.xw[j] = load_buf<Act>(rx, xo[j]);
+    for (int j = 0; j < TPL + 3; ++j) in.xw[j] = load_raw_t<Act>(rx, xoff[j]);
 #pragma unroll
     for (int r = 0; r < TPL; ++r) {
-      in.dr[r] = load_buf<Act>(rd, to[r]);
-      if constexpr (!kCarry) in.zz[r] = load_buf<Act>(rz, to[r]);
+      in.dr[r] = load_raw_t<Act>(rd, xoff_t[r]);
+      if constexpr (!kCarry) in.zz[r] = load_raw_t<Act>(rz, xoff_t[r]);
     }
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
-      in.RB[j] = load_buf<Act>(rB, bo[j]);
-      if constexpr (!kCarry) in.RC[j] = load_buf<Act>(rC, bo[j]);
-    }
-  };
-  auto load_tile = [&](int64_t ts, TileIn<TPL, NR>& in) {
-    if (ts + kTile <= L) {
-      load_seq(ts, in, xoff, xoff_t, bcoff);
-    } else {
-      const int lim = static_cast<int>(L - 1 - ts);  // last token of the sequence, tile-relative
-      const uint32_t e32 = static_cast<uint32_t>(e);
-      uint32_t xo[TPL + 3], to[TPL], bo[NR];
-#pragma unroll
-      for (int j = 0; j < TPL + 3; ++j)
-        xo[j] = (static_cast<uint32_t>(min(tau0 + j - 3, lim) + 3) * E32 + e32) * kElt;
-#pragma unroll
-      for (int r = 0; r < TPL; ++r)
-        to[r] = (static_cast<uint32_t>(min(tau0 + r, lim)) * E32 + e32) * kElt;
-#pragma unroll
-      for (int j = 0; j < NR; ++j)
-        bo[j] = static_cast<uint32_t>(min(j * TPR + c / SPL, lim) * kState + g * SPL + (c % SPL)) *
-                kElt;
-      load_seq(ts, in, xo, to, bo);
+      in.RB[j] = load_raw_t<Act>(rB, bcoff[j]);
+      if constexpr (!kCarry) in.RC[j] = load_raw_t<Act>(rC, bcoff[j]);
     }
   };
   // Tokens past the chunk end (and lanes past the last channel) get dt = 0: their state update
   // is the identity.
-  auto prologue = [&](int64_t ts, const TileIn<TPL, NR>& in, int buf, float (&u)[TPL]) {
+  auto prologue = [&](int64_t ts, const float (&xw)[TPL + 3], const Tile& in, int buf,
+                      float (&u)[TPL]) {
     const int rem = static_cast<int>(te - ts < kTile ? te - ts : kTile);  // tokens in the chunk
     float pair[2 * TPL];
 #pragma unroll
     for (int r = 0; r < TPL; ++r) {
-      float uu = fmaf(w3, in.xw[r + 3],
-                      fmaf(w2, in.xw[r + 2], fmaf(w1, in.xw[r + 1], fmaf(w0, in.xw[r], cb))));
+      float uu = fmaf(w3, xw[r + 3], fmaf(w2, xw[r + 2], fmaf(w1, xw[r + 1], fmaf(w0, xw[r], cb))));
       if constexpr (kSilu) uu = silu(uu);
       const float keep = (valid && tau0 + r < rem) ? 1.0f : 0.0f;
-      const float dt = step_size(in.dr[r] + dtb, a.dt_min, a.dt_max) * keep;
+      const float dt = step_size(widen(in.dr[r]) + dtb, a.dt_min, a.dt_max) * keep;
       pair[2 * r] = dt;
       pair[2 * r + 1] = kZoh ? uu : dt * uu;  // the exact hold scales u per state in the scan
       u[r] = uu;
@@ -567,18 +565,21 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
   // while tile k is scanned, tile k+1's inputs wait for their prologue and tile k+2's are in
   // flight. The main loop handles whole triples of tiles with the slots' roles rotated, so
   // loaded registers are never copied (a copy would wait for its load).
-  TileIn<TPL, NR> ring0, ring1, ring2;
+  Tile ring0, ring1, ring2;
   float u_cur[TPL];
-  load_tile_first(tb, ring0);
-  if (ntiles > 1) load_tile_first(tb + kTile, ring1);
-  prologue(tb, ring0, 0, u_cur);
+  float x0[TPL + 3];
+#pragma unroll
+  for (int j = 0; j < TPL + 3; ++j) x0[j] = load_x(tb + tau0 - 3 + j);
+  load_tile_first(tb, ring0, false);
+  if (ntiles > 1) load_tile_first(tb + kTile, ring1, true);
+  prologue(tb, x0, ring0, 0, u_cur);
   __syncthreads();
 
   float S = 0.0f;
   // Tile k: scan with cur's B / C, prologue of tile k+1 from nxt, epilogue with cur's z; with
   // kLoad, tile k+2 (clamped to the last tile) is first loaded into fut.
-  auto do_tile = [&](auto load_tag, int64_t k, const TileIn<TPL, NR>& cur,
-                     const TileIn<TPL, NR>& nxt, TileIn<TPL, NR>& fut) {
+  auto do_tile = [&](auto load_tag, int64_t k, const Tile& cur,
+                     const Tile& nxt, Tile& fut) {
     constexpr bool kLoad = decltype(load_tag)::value;
     const int64_t ts = tb + k * kTile;
     const int buf = static_cast<int>(k & 1);
@@ -587,16 +588,26 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
 #pragma unroll
     for (int i = 0; i < kTile / 2; ++i)
       dd[i] = *reinterpret_cast<const float4*>(&s_dt[buf][slot][4 * i]);
-    float P[kTile], ac[SPL];
+    float P[kTile], ac[SPL], RB[NR], RC[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      RB[j] = widen(cur.RB[j]);
+      RC[j] = kCarry ? 0.0f : widen(cur.RC[j]);
+    }
     if constexpr (kZoh) {
       float yc[SPL];
-      scan_tile_zoh_from<SPL, kCarry, 0, kTile>(dd, rate, ia, zc, cur.RB, cur.RC, h, ac, yc, P, S);
+      scan_tile_zoh_from<SPL, kCarry, 0, kTile>(dd, rate, ia, zc, RB, RC, h, ac, yc, P, S);
     } else {
-      scan_tile_from<SPL, kCarry, 0, kTile>(dd, rate, cur.RB, cur.RC, h, ac, P, S);
+      scan_tile_from<SPL, kCarry, 0, kTile>(dd, rate, RB, RC, h, ac, P, S);
     }
 
     float u_next[TPL];
-    if (k + 1 < ntiles) prologue(ts + kTile, nxt, buf ^ 1, u_next);
+    if (k + 1 < ntiles) {
+      float xw[TPL + 3];
+#pragma unroll
+      for (int j = 0; j < TPL + 3; ++j) xw[j] = widen(nxt.xw[j]);
+      prologue(ts + kTile, xw, nxt, buf ^ 1, u_next);
+    }
     if constexpr (!kCarry) {
       // Row q of the reduced register for tokens 4x .. 4x+3 holds token 4x + q.
 #pragma unroll
@@ -619,7 +630,7 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
         float ysum = s_ex[buf][grp * W][ix];
 #pragma unroll
         for (int v = 1; v < W; ++v) ysum += s_ex[buf][grp * W + v][ix];
-        const float yv = fmaf(Dv, u_cur[r], ysum) * silu(cur.zz[r]);
+        const float yv = fmaf(Dv, u_cur[r], ysum) * silu(widen(cur.zz[r]));
         store_buf<Act>(ry, yoff[r], yv);
       }
     }
