@@ -367,8 +367,11 @@ struct TileIn {
 };
 
 // kSilu: SiLU on the convolution output (Mamba-block variant); kZoh: exact zero-order hold.
+// The two-states-per-lane final pass fits 128 VGPRs with no spill in its loop, which gives
+// it 4 waves per SIMD instead of 3.
 template <typename Act, int W, bool kCarry, bool kSilu, bool kZoh>
-__global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
+__global__ __launch_bounds__(64 * W * kGroups) __attribute__((
+    amdgpu_waves_per_eu(W == 2 && !kCarry && !kZoh ? 4 : 1))) void row_scan_kernel(RowArgs a) {
   constexpr int SPL = 4 / W;  // states per lane
   constexpr int kTile = tile_tokens<W>();
   constexpr int kDtStride = 2 * kTile + 4;  // floats per channel in the dt / dtu tile (padded)
@@ -509,20 +512,17 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
   const Act* const zrow = zp + b * L * E;
   Act* const yrow = yp + b * L * E;
   const uint32_t tile_row = static_cast<uint32_t>(E * kElt);  // bytes per token of a stream
-  auto range = [](int64_t tokens, int64_t token_bytes) -> uint32_t {
-    const int64_t bytes = tokens * token_bytes;
-    return bytes < 0xffffffffLL ? static_cast<uint32_t>(bytes) : 0xffffffffu;
-  };
   auto load_tile = [&](int64_t ts, Tile& in) {
     const int64_t toff = ts * E;
-    const int64_t left = L - ts;  // tokens from the tile's first to the end of the sequence
-    const rsrc_t rx = make_rsrc_bounded(const_cast<Act*>(xrow + toff), range(left + 3, tile_row));
-    const rsrc_t rd = make_rsrc_bounded(const_cast<Act*>(drow + toff), range(left, tile_row));
-    const rsrc_t rz = make_rsrc_bounded(const_cast<Act*>(zrow + toff), range(left, tile_row));
-    const rsrc_t rB =
-        make_rsrc_bounded(const_cast<Act*>(Bp + ts * kState), range(left, kState * kElt));
-    const rsrc_t rC =
-        make_rsrc_bounded(const_cast<Act*>(Cp + ts * kState), range(left, kState * kElt));
+    // Tokens of the tile inside the sequence (its offsets reach no further than kTile tokens
+    // past its first, 3 more for x; the byte counts fit 32 bits as the host bounds d_inner).
+    const uint32_t n = static_cast<uint32_t>(L - ts < kTile ? L - ts : kTile);
+    const uint32_t bc_row = static_cast<uint32_t>(kState * kElt);
+    const rsrc_t rx = make_rsrc_bounded(const_cast<Act*>(xrow + toff), (n + 3) * tile_row);
+    const rsrc_t rd = make_rsrc_bounded(const_cast<Act*>(drow + toff), n * tile_row);
+    const rsrc_t rz = make_rsrc_bounded(const_cast<Act*>(zrow + toff), n * tile_row);
+    const rsrc_t rB = make_rsrc_bounded(const_cast<Act*>(Bp + ts * kState), n * bc_row);
+    const rsrc_t rC = make_rsrc_bounded(const_cast<Act*>(Cp + ts * kState), n * bc_row);
 #pragma unroll
     for (int j = 0; j < TPL + 3; ++j) in.xw[j] = load_raw_t<Act>(rx, xoff[j]);
 #pragma unroll
@@ -558,6 +558,10 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
           make_float4(pair[2 * r], pair[2 * r + 1], pair[2 * r + 2], pair[2 * r + 3]);
   };
   auto ex_index = [&](int tau) { return tau * 16 + c + 16 * (tau / TPL); };
+  // Token 4 x4 + q of the four-row sums goes to ex_index(q) plus a constant of x4 (TPL divides
+  // 4 or 4 divides TPL), which the compiler folds into the LDS store's offset.
+  static_assert(4 % TPL == 0 || TPL % 4 == 0, "reduced-token index split");
+  const int ex_q = ex_index(q);
 
   const int64_t ntiles = (te - tb + kTile - 1) / kTile;
   const int64_t ts_last = tb + (ntiles - 1) * kTile;
@@ -613,7 +617,7 @@ __global__ __launch_bounds__(64 * W * kGroups) void row_scan_kernel(RowArgs a) {
 #pragma unroll
       for (int x4 = 0; x4 < 4 * NX; ++x4) {
         const float R = rows_reduce4(P[4 * x4], P[4 * x4 + 1], P[4 * x4 + 2], P[4 * x4 + 3]);
-        s_ex[buf][wid][ex_index(4 * x4 + q)] = R;
+        s_ex[buf][wid][ex_q + 64 * x4 + 16 * (4 * x4 / TPL)] = R;
       }
     }
     __syncthreads();
