@@ -18,9 +18,10 @@
 // Four kernels, in stream order:
 //   ssd_gram_kernel   G_c = C_c B_c^T (64 x 64, lower block triangle), shared by all heads.
 //   ssd_state_kernel  S_c for every (b, h, c) and the chunk decay exp(cum_last).
-//   ssd_pass_kernel   the recurrence over chunks, in place: S_c is replaced by H_c; the final
-//                     state goes to state_out.
-//   ssd_output_kernel y for every (b, h, c) from H_c, G_c and x.
+//   ssd_carry_kernel  the recurrence over chunks with H_c held on chip, and for every chunk the
+//                     incoming-state products C_t . H_c[p] (unscaled); the final state goes to
+//                     state_out. H_c itself is never stored.
+//   ssd_output_kernel y for every (b, h, c) from those products, G_c and x.
 // The contractions run on v_mfma_f32_16x16x4f32 (fp32 in, fp32 accumulate). Operand layout of
 // that instruction (wave64, lane l, g = l / 16, i = l % 16): A supplies A[i][k = g], B supplies
 // B[k = g][i], and the 16 x 16 result sits as D[4 g + r][i] in the r-th of 4 accumulators. Any
@@ -50,9 +51,11 @@ struct SsdArgs {
   const float* state_in;
   void* y;
   float* state_out;
-  float* states;  // (B, H, nc, P, N): S_c, replaced by H_c in the pass kernel
+  float* states;  // (B, H, nc, P, N): S_c
   float* decay;   // (B, H, nc): exp(cum_last) of each chunk
   float* gram;    // (B, nc, Q, Q): C_c B_c^T
+  float* yinter;  // (B, H, nc, 2, Q, P): sum_n C_t[n] H_c[p, n] over each half of the states
+                  // (before the exp2(cum_t) factor)
   int64_t seqlen, heads;
   int nchunks;
 };
@@ -227,38 +230,113 @@ __global__ __launch_bounds__(kThreads * HG) void ssd_state_kernel(SsdArgs a) {
         make_float4(acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]);
 }
 
-// ---- recurrence over chunks -----------------------------------------------------------------
-// Grid (P N / 4 / 256, H, B): one float4 of the (P, N) state per thread. In place: slot c of
-// the states buffer holds S_c on entry and H_c (the state entering chunk c) on exit. The loads
-// of 8 chunks are issued together, so one memory latency covers 8 steps of the recurrence.
-__global__ __launch_bounds__(kThreads) void ssd_pass_kernel(SsdArgs a) {
-  constexpr int kVec = kP * kN / 4;
-  constexpr int kDepth = 8;
-  const int i4 = blockIdx.x * kThreads + threadIdx.x;
-  const int64_t bh = int64_t(blockIdx.z) * a.heads + blockIdx.y;
-  float4 hs = a.state_in ? reinterpret_cast<const float4*>(a.state_in)[bh * kVec + i4]
-                         : float4{0.0f, 0.0f, 0.0f, 0.0f};
-  float4* S = reinterpret_cast<float4*>(a.states + bh * a.nchunks * int64_t(kP * kN)) + i4;
-  const float* dec = a.decay + bh * a.nchunks;
-  for (int c0 = 0; c0 < a.nchunks; c0 += kDepth) {
-    const int n = a.nchunks - c0 < kDepth ? a.nchunks - c0 : kDepth;
-    float4 v[kDepth];
+// ---- recurrence over chunks and the incoming-state products -------------------------------
+// Grid (2 P / 16, H, B), 4 waves. A workgroup owns head channels p0 .. p0 + 15 of one (b, h) and
+// one half of the states, n0 .. n0 + 63, and walks the chunks in order with that block of the
+// state in registers. Every wave keeps the whole block (lane (g, i): channel p0 + i, states
+// n0 + 16 k + 4 g .. + 3 for k = 0..3), so the waves exchange nothing. For chunk c, wave w
+// contracts the C rows of tokens 16 w .. 16 w + 15 with H_c over the block's 64 states (A operand
+// C, B operand H^T, contraction index n0 + 16 k + 4 g + q at k-step (k, q), one accumulator per
+// q: a 16-byte load per lane and k reads 64 contiguous bytes of each row), writes these partial
+// products (the output kernel adds the two halves) to the workspace, and then advances the state:
+// H_{c+1} = exp(cum_last of c) H_c + S_c. The next chunk's C rows and S slice are loaded while
+// the current chunk is contracted (two register sets, chunks taken in pairs).
+template <typename Act>
+__global__ __launch_bounds__(kThreads) void ssd_carry_kernel(SsdArgs a) {
+  const int64_t h = blockIdx.y, b = blockIdx.z;
+  const int p0 = 16 * static_cast<int>(blockIdx.x >> 1), half = blockIdx.x & 1, n0 = 64 * half;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
+  const int64_t bh = b * a.heads + h;
+  const Act* Cp = static_cast<const Act*>(a.C);
+  const int64_t srow = (bh * kP + p0 + i) * kN + n0 + 4 * g;  // this lane's part of a state
+  float hs[16];
 #pragma unroll
-    for (int k = 0; k < kDepth; ++k)
-      if (k < n) v[k] = S[int64_t(c0 + k) * kVec];
-#pragma unroll
-    for (int k = 0; k < kDepth; ++k) {
-      if (k < n) {
-        S[int64_t(c0 + k) * kVec] = hs;
-        const float d = dec[c0 + k];
-        hs.x = fmaf(d, hs.x, v[k].x);
-        hs.y = fmaf(d, hs.y, v[k].y);
-        hs.z = fmaf(d, hs.z, v[k].z);
-        hs.w = fmaf(d, hs.w, v[k].w);
-      }
-    }
+  for (int k = 0; k < 4; ++k) {
+    const float4 v = a.state_in ? *reinterpret_cast<const float4*>(a.state_in + srow + 16 * k)
+                                : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    hs[4 * k] = v.x, hs[4 * k + 1] = v.y, hs[4 * k + 2] = v.z, hs[4 * k + 3] = v.w;
   }
-  reinterpret_cast<float4*>(a.state_out)[bh * kVec + i4] = hs;
+  // Every wave has read its state before wave 0 may write state_out (which may be state_in).
+  __syncthreads();
+  // S_c is read from memory once per workgroup: thread t loads 16 bytes of row p0 + t / 16 and
+  // stores them in LDS where lane (g, i) of every wave reads its k-th float4 (slot 64 k + lane),
+  // two chunk buffers alternating. (C rows go straight to registers: staged through LDS as well
+  // they took 64 us instead of 43 us at 1 x 2048 x 64 heads.)
+  __shared__ float4 ssh[2][4 * 64];
+  const int prow = tid >> 4, pch = tid & 15;
+  const float* Sg = a.states + bh * a.nchunks * int64_t(kP * kN) + (p0 + prow) * kN + n0 + 4 * pch;
+  const int sdst = (pch >> 2) * 64 + 16 * (pch & 3) + prow;
+  float* Y0 = a.yinter + (bh * a.nchunks * 2 + half) * int64_t(kQ * kP) + (16 * w + 4 * g) * kP +
+              p0 + i;
+  const float* dec = a.decay + bh * a.nchunks;
+  // A chunk's inputs: its C rows, this thread's part of its S block and its decay, loaded a chunk
+  // ahead of use (the decay with them: loaded next to its use, its wait would also wait for the
+  // prefetch).
+  auto load = [&](int c, float4 (&cr)[4], float4& sg, float& d) {
+    // S first: its LDS store at the end of the current chunk then waits for it alone.
+    d = dec[c];
+    sg = *reinterpret_cast<const float4*>(Sg + int64_t(c) * (kP * kN));
+    // Tokens past the sequence end take the last token's C row (their products are never read),
+    // so every lane issues the same loads and the compiler's wait counts stay exact.
+    const int64_t tok = int64_t(c) * kQ + 16 * w + i;
+    const int64_t row = (b * a.seqlen + (tok < a.seqlen ? tok : a.seqlen - 1)) * kN + n0 + 4 * g;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cr[k] = load4(Cp, row + 16 * k);
+  };
+  auto chunk = [&](int c, const float4 (&cr)[4], float d, const float4* sb) {
+    float4 sr[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sr[k] = sb[64 * k + lane];
+    f4 acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[0] = mfma4(cr[k].x, hs[4 * k], acc[0]);
+      acc[1] = mfma4(cr[k].y, hs[4 * k + 1], acc[1]);
+      acc[2] = mfma4(cr[k].z, hs[4 * k + 2], acc[2]);
+      acc[3] = mfma4(cr[k].w, hs[4 * k + 3], acc[3]);
+    }
+    float* Y = Y0 + int64_t(c) * (2 * kQ * kP);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Y[r * kP] = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      hs[4 * k] = fmaf(d, hs[4 * k], sr[k].x);
+      hs[4 * k + 1] = fmaf(d, hs[4 * k + 1], sr[k].y);
+      hs[4 * k + 2] = fmaf(d, hs[4 * k + 2], sr[k].z);
+      hs[4 * k + 3] = fmaf(d, hs[4 * k + 3], sr[k].w);
+    }
+  };
+  float4 c0[4], c1[4], g0, g1;
+  float d0, d1;
+  // Prefetches past the last chunk reload the last chunk (unused), so no load sits behind a
+  // branch; the scheduling barriers keep each prefetch ahead of the chunk it overlaps. Each
+  // chunk's S block is in LDS before the chunk starts; the barrier after a buffer is filled also
+  // orders the previous reads of that buffer before its next fill.
+  const int last = a.nchunks - 1;
+  load(0, c0, g0, d0);
+  ssh[0][sdst] = g0;
+  __syncthreads();
+  for (int c = 0; c < a.nchunks; c += 2) {
+    load(c + 1 < last ? c + 1 : last, c1, g1, d1);
+    __builtin_amdgcn_sched_barrier(0);
+    chunk(c, c0, d0, ssh[0]);
+    ssh[1][sdst] = g1;
+    __syncthreads();
+    if (c + 1 > last) break;
+    load(c + 2 < last ? c + 2 : last, c0, g0, d0);
+    __builtin_amdgcn_sched_barrier(0);
+    chunk(c + 1, c1, d1, ssh[1]);
+    ssh[0][sdst] = g0;
+    __syncthreads();
+  }
+  if (w == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<float4*>(a.state_out + srow + 16 * k) =
+          make_float4(hs[4 * k], hs[4 * k + 1], hs[4 * k + 2], hs[4 * k + 3]);
+  }
 }
 
 // state_out = state_in (or zeros) for an empty sequence.
@@ -272,20 +350,15 @@ __global__ __launch_bounds__(kThreads) void ssd_copy_state_kernel(const float* i
 
 // ---- outputs ---------------------------------------------------------------------------------
 // Grid (nc, H, B), 4 waves; wave w owns tokens 16 w .. 16 w + 15 of the chunk and all 64 head
-// channels (4 column blocks). H_c (64 x 128) is staged in LDS once per workgroup (row stride
-// 132 floats: the 16 rows of one 16-byte LDS read fall in distinct banks); the C rows of the
-// wave's tokens come straight from global memory. Incoming-state term: contraction over the
-// states, then each row scaled by exp2(cum_t). Intra-chunk term: contraction over
-// s = 16 st + 4 g + j for the column blocks st <= w, the A operand being G scaled by the decay
-// mask, the B operand x from LDS (row stride 68 floats: the four lane groups, 4 rows apart,
-// hit disjoint banks).
+// channels (4 column blocks). Intra-chunk term: contraction over s = 16 st + 4 g + j for the
+// column blocks st <= w, the A operand being G scaled by the decay mask, the B operand x from
+// LDS (row stride 68 floats: the four lane groups, 4 rows apart, hit disjoint banks).
+// Incoming-state term: the carry kernel's products C_t . H_c[p], scaled by exp2(cum_t).
 constexpr int kXO = kP + 4;
-constexpr int kHO = kN + 4;
 
 template <typename Act>
 __global__ __launch_bounds__(kThreads) void ssd_output_kernel(SsdArgs a) {
   __shared__ float xs[kQ * kXO];
-  __shared__ float hsm[kP * kHO];
   __shared__ float cum_hi[kQ];
   __shared__ float cum_lo[kQ];
   __shared__ float dts[kQ];
@@ -312,44 +385,26 @@ __global__ __launch_bounds__(kThreads) void ssd_output_kernel(SsdArgs a) {
                           : float4{};
       *reinterpret_cast<float4*>(&xs[t * kXO + 16 * q + j]) = v;
     }
-    // H_c: thread -> channel tid / 4, states 32 (tid % 4) .. + 31
-    const float* Hc = a.states + (bh * a.nchunks + c) * int64_t(kP * kN) + t * kN + 32 * q;
-#pragma unroll
-    for (int j = 0; j < 32; j += 4)
-      *reinterpret_cast<float4*>(&hsm[t * kHO + 32 * q + j]) =
-          *reinterpret_cast<const float4*>(Hc + j);
   }
-  float4 crow[8];
+  // The incoming-state products of this lane's outputs (token 16 w + 4 g + r, channel 16 pt + i).
+  float yin[4][4];
   {
-    const int64_t tok = tok0 + 16 * w + i;
-    const bool ok = tok < a.seqlen;
-    const Act* Cp = static_cast<const Act*>(a.C);
+    const float* Yi = a.yinter + (bh * a.nchunks + c) * int64_t(2 * kQ * kP) +
+                      (16 * w + 4 * g) * kP + i;
 #pragma unroll
-    for (int jb = 0; jb < 8; ++jb)
-      crow[jb] = ok ? load4(Cp, (b * a.seqlen + tok) * kN + 16 * jb + 4 * g) : float4{};
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+        yin[r][pt] = Yi[r * kP + 16 * pt] + Yi[kQ * kP + r * kP + 16 * pt];
   }
-  __syncthreads();  // xs, hsm, cum_hi, cum_lo, dts ready
+  __syncthreads();  // xs, cum_hi, cum_lo, dts ready
   f4 acc[4];
-#pragma unroll
-  for (int pt = 0; pt < 4; ++pt) acc[pt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int jb = 0; jb < 8; ++jb) {
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      const float4 hv = *reinterpret_cast<const float4*>(&hsm[(16 * pt + i) * kHO + 16 * jb +
-                                                               4 * g]);
-      acc[pt] = mfma4(crow[jb].x, hv.x, acc[pt]);
-      acc[pt] = mfma4(crow[jb].y, hv.y, acc[pt]);
-      acc[pt] = mfma4(crow[jb].z, hv.z, acc[pt]);
-      acc[pt] = mfma4(crow[jb].w, hv.w, acc[pt]);
-    }
-  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = 16 * w + 4 * g + r;
     const float e = __builtin_amdgcn_exp2f(cum_hi[t] + cum_lo[t]);
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) acc[pt][r] *= e;
+    for (int pt = 0; pt < 4; ++pt) acc[pt][r] = e * yin[r][pt];
   }
   {
     const int t = 16 * w + i;  // A-operand row
@@ -391,7 +446,7 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 struct SsdPlan {
   int64_t nchunks = 0;
-  size_t off_states = 0, off_decay = 0, off_gram = 0, bytes = 0;
+  size_t off_states = 0, off_decay = 0, off_gram = 0, off_yinter = 0, bytes = 0;
 };
 
 size_t round_up(size_t v, size_t m) { return (v + m - 1) / m * m; }
@@ -422,7 +477,8 @@ SsdPlan plan_ssd(const axon_ssd_shape* s) {
   p.off_states = 0;
   p.off_decay = round_up(p.off_states + sizeof(float) * BH * p.nchunks * kP * kN, 256);
   p.off_gram = round_up(p.off_decay + sizeof(float) * BH * p.nchunks, 256);
-  p.bytes = round_up(p.off_gram + sizeof(float) * size_t(s->batch) * p.nchunks * kQ * kQ, 256);
+  p.off_yinter = round_up(p.off_gram + sizeof(float) * size_t(s->batch) * p.nchunks * kQ * kQ, 256);
+  p.bytes = round_up(p.off_yinter + sizeof(float) * BH * p.nchunks * 2 * kQ * kP, 256);
   return p;
 }
 
@@ -453,7 +509,7 @@ void launch_all(const SsdArgs& a, int64_t batch, hipStream_t st) {
                        a);
   else
     hipLaunchKernelGGL((ssd_state_kernel<Act, 1>), dim3(nc, H, B), blk, 0, st, a);
-  hipLaunchKernelGGL(ssd_pass_kernel, dim3(kP * kN / 4 / kThreads, H, B), blk, 0, st, a);
+  hipLaunchKernelGGL(ssd_carry_kernel<Act>, dim3(2 * kP / 16, H, B), blk, 0, st, a);
   hipLaunchKernelGGL(ssd_output_kernel<Act>, dim3(nc, H, B), blk, 0, st, a);
 }
 
@@ -531,6 +587,7 @@ axon_status axon_ssd_scan(const axon_ssd_shape* shape, const axon_ssd_params* pa
   a.states = reinterpret_cast<float*>(w + plan.off_states);
   a.decay = reinterpret_cast<float*>(w + plan.off_decay);
   a.gram = reinterpret_cast<float*>(w + plan.off_gram);
+  a.yinter = reinterpret_cast<float*>(w + plan.off_yinter);
   a.seqlen = L, a.heads = H, a.nchunks = static_cast<int>(plan.nchunks);
   if (shape->act_dtype == AXON_BF16)
     launch_all<bf16_bits>(a, Bsz, st);
