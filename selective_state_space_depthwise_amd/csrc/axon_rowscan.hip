@@ -37,7 +37,14 @@
 namespace axon {
 namespace {
 
-constexpr int kGroups = 2;  // 16-channel groups per workgroup
+// 16-channel groups per workgroup. One where a lane holds one state: four-wave workgroups, two
+// per CU, so the two waves of a SIMD belong to workgroups that meet their barriers independently
+// (1 x 2048 x 7680 fp32: 1-1.5% faster per launch than two groups, 4% with inputs in the
+// last-level cache). Two otherwise (8 x 4096 x 7680 bf16 with one group: 7% slower).
+template <int W>
+constexpr int groups() {
+  return W == 4 ? 1 : 2;
+}
 
 // Tokens per tile: 32 where a lane holds one state (more work between barriers), 16 otherwise
 // (the register budget of 4 states per lane).
@@ -370,12 +377,13 @@ struct TileIn {
 // The two-states-per-lane final pass fits 128 VGPRs with no spill in its loop, which gives
 // it 4 waves per SIMD instead of 3.
 template <typename Act, int W, bool kCarry, bool kSilu, bool kZoh>
-__global__ __launch_bounds__(64 * W * kGroups) __attribute__((
+__global__ __launch_bounds__(64 * W * groups<W>()) __attribute__((
     amdgpu_waves_per_eu(W == 2 && !kCarry && !kZoh ? 4 : 1))) void row_scan_kernel(RowArgs a) {
   constexpr int SPL = 4 / W;  // states per lane
   constexpr int kTile = tile_tokens<W>();
   constexpr int kDtStride = 2 * kTile + 4;  // floats per channel in the dt / dtu tile (padded)
   constexpr int TPL = kTile / (4 * W);      // prologue / epilogue tokens per lane per tile
+  constexpr int kGroups = groups<W>();
   constexpr int NW = W * kGroups;
   constexpr int TPR = 16 / SPL;         // tokens per B / C register
   constexpr int NR = kTile * SPL / 16;  // B / C registers per tile
@@ -682,6 +690,7 @@ void launch_carry_combine(int64_t B, int64_t E, int64_t M, const float* A_log,
 
 template <typename Act, int W, bool kSilu, bool kZoh>
 int launch_row_scan_t(const PrefillLaunch& p, const PrefillPlan& plan, hipStream_t s) {
+  constexpr int kGroups = groups<W>();
   RowArgs a{};
   a.B = p.batch;
   a.L = p.seqlen;
