@@ -574,7 +574,9 @@ MICRO_KINDS = ["fma", "exp", "dpp_row_newbcast_mul", "permlane32_swap", "state_u
                "permlane16_swap", "exp_1_per_1_fma", "exp_1_per_2_fma", "exp_1_per_8_fma",
                "lane_per_channel_update", "lane_per_channel_update_exp_as_mul",
                "16_exp_then_48_fma", "8_exp_then_24_fma_twice", "16_exp_then_48_fma_vop3",
-               "fma_sgpr_operand"]
+               "fma_sgpr_operand", "one_chain_update_exp_read_2_later",
+               "one_chain_update_decay_one_token_ahead", "one_chain_exps_grouped_then_dpp",
+               "one_chain_exps_grouped_then_plain"]
 
 
 def bench_micro():

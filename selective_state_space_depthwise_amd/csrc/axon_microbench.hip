@@ -36,7 +36,13 @@ enum Kind : int {
   kBurst8 = 16,    // 8 v_exp_f32, then 24 v_fmac_f32
   kBurst16v3 = 17, // 16 v_exp_f32, then 48 v_fma_f32 (VOP3)
   kFmaSgpr = 18,   // 8 independent v_fmac_f32 chains with one operand in an SGPR
-  kNumKinds = 19
+  // One state chain per lane, 8 tokens per block (the row scan with one state per lane):
+  kChainDpp = 19,    // per token: mul, exp, DPP input product, DPP readout product, fma
+                     // (the exp's result read two instructions later)
+  kChainAhead = 20,  // the same with the decay computed one token ahead (the kernel's order)
+  kPhaseDpp = 21,    // the 8 tokens' mul and exp first, then their DPP products and fmas
+  kPhasePlain = 22,  // the same with B and C as plain registers instead of DPP broadcasts
+  kNumKinds = 23
 };
 
 // VALU instructions per loop iteration of each kind (the SALU of kFmaSalu not counted).
@@ -46,7 +52,8 @@ __host__ __device__ constexpr int instrs_per_iter(int kind) {
        : kind == kFmaChain ? 32 : kind == kExpChain ? 32 : kind == kPerm16 ? 64
        : kind == kExpFma1 ? 64 : kind == kExpFma2 ? 72 : kind == kExpFma8 ? 72
        : kind == kChanUpd ? 80 : kind == kChanNoExp ? 80 : kind == kBurst16 ? 64
-       : kind == kBurst8 ? 64 : kind == kBurst16v3 ? 64 : kind == kFmaSgpr ? 64 : 0;
+       : kind == kBurst8 ? 64 : kind == kBurst16v3 ? 64 : kind == kFmaSgpr ? 64
+       : kind >= kChainDpp && kind <= kPhasePlain ? 80 : 0;
 }
 
 #define F8(op) op(0) op(1) op(2) op(3) op(4) op(5) op(6) op(7)
@@ -247,6 +254,57 @@ __global__ __launch_bounds__(1024) void alu_kernel(int iters, float seed, float*
 #undef BE8P
 #undef BE8
 #undef BE
+    } else if constexpr (kKind >= kChainDpp && kKind <= kPhasePlain) {
+      // h[0] is the state, h[1] the input product, nn[] the decays, p[] the readout products,
+      // b[] the plain B registers; B, C and dtu (a[0..2]) are never written.
+#define CA(i) "v_mul_f32 %[n" #i "], %[dt], %[r]\n\t"
+#define CE(i) "v_exp_f32 %[n" #i "], %[n" #i "]\n\t"
+#define CB "v_mul_f32_dpp %[bb], %[RB], %[dtu] row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+#define CC(i) "v_mul_f32_dpp %[p" #i "], %[RC], %[h] row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+#define CF(i) "v_fma_f32 %[h], %[n" #i "], %[h], %[bb]\n\t"
+#define PB(i) "v_mul_f32 %[bb], %[R" #i "], %[dtu]\n\t"
+#define PC(i) "v_mul_f32 %[p" #i "], %[RC], %[h]\n\t"
+#define CHAIN(i) CA(i) CE(i) CB CC(i) CF(i)
+#define AHEAD(i, j) CA(j) CE(j) CB CC(i) CF(i)
+#define PHD(i) CB CC(i) CF(i)
+#define PHP(i) PB(i) PC(i) CF(i)
+#define COUT [n0] "+v"(nn[0]), [n1] "+v"(nn[1]), [n2] "+v"(nn[2]), [n3] "+v"(nn[3]), \
+             [n4] "+v"(nn[4]), [n5] "+v"(nn[5]), [n6] "+v"(nn[6]), [n7] "+v"(nn[7]), \
+             [p0] "+v"(p[0]), [p1] "+v"(p[1]), [p2] "+v"(p[2]), [p3] "+v"(p[3]), \
+             [p4] "+v"(p[4]), [p5] "+v"(p[5]), [p6] "+v"(p[6]), [p7] "+v"(p[7]), \
+             [h] "+v"(h[0]), [bb] "+v"(h[1])
+#define CIN [dt] "v"(m), [r] "v"(n), [RB] "v"(a[0]), [RC] "v"(a[1]), [dtu] "v"(a[2]), \
+            [R0] "v"(b[0]), [R1] "v"(b[1]), [R2] "v"(b[2]), [R3] "v"(b[3]), [R4] "v"(b[4]), \
+            [R5] "v"(b[5]), [R6] "v"(b[6]), [R7] "v"(b[7])
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if constexpr (kKind == kChainDpp) {
+          asm volatile(CHAIN(0) CHAIN(1) CHAIN(2) CHAIN(3) CHAIN(4) CHAIN(5) CHAIN(6) CHAIN(7)
+                       : COUT : CIN);
+        } else if constexpr (kKind == kChainAhead) {
+          asm volatile(AHEAD(0, 1) AHEAD(1, 2) AHEAD(2, 3) AHEAD(3, 4) AHEAD(4, 5) AHEAD(5, 6)
+                       AHEAD(6, 7) AHEAD(7, 0) : COUT : CIN);
+        } else if constexpr (kKind == kPhaseDpp) {
+          asm volatile(F8(CA) F8(CE) "s_nop 1\n\t" PHD(0) PHD(1) PHD(2) PHD(3) PHD(4) PHD(5)
+                       PHD(6) PHD(7) : COUT : CIN);
+        } else {
+          asm volatile(F8(CA) F8(CE) PHP(0) PHP(1) PHP(2) PHP(3) PHP(4) PHP(5) PHP(6) PHP(7)
+                       : COUT : CIN);
+        }
+      }
+#undef CIN
+#undef COUT
+#undef PHP
+#undef PHD
+#undef AHEAD
+#undef CHAIN
+#undef PC
+#undef PB
+#undef CF
+#undef CC
+#undef CB
+#undef CE
+#undef CA
     } else if constexpr (kKind == kFmaSalu) {
       unsigned s0 = it, s1 = it + 1;
 #define FS(i) FMA1(i) "s_add_u32 %[s0], %[s0], %[s1]\n\t"
@@ -429,6 +487,10 @@ int axon_micro_alu(int kind, int waves_per_simd, int iters, double* out) {
       case kBurst8: return launch_alu<kBurst8>(waves_per_simd, it, sink, clocks, nullptr);
       case kBurst16v3: return launch_alu<kBurst16v3>(waves_per_simd, it, sink, clocks, nullptr);
       case kFmaSgpr: return launch_alu<kFmaSgpr>(waves_per_simd, it, sink, clocks, nullptr);
+      case kChainDpp: return launch_alu<kChainDpp>(waves_per_simd, it, sink, clocks, nullptr);
+      case kChainAhead: return launch_alu<kChainAhead>(waves_per_simd, it, sink, clocks, nullptr);
+      case kPhaseDpp: return launch_alu<kPhaseDpp>(waves_per_simd, it, sink, clocks, nullptr);
+      case kPhasePlain: return launch_alu<kPhasePlain>(waves_per_simd, it, sink, clocks, nullptr);
       default: return launch_alu<kPerm16>(waves_per_simd, it, sink, clocks, nullptr);
     }
   };
