@@ -54,7 +54,7 @@ struct SsdArgs {
   float* states;  // (B, H, nc, P, N): S_c
   float* decay;   // (B, H, nc): exp(cum_last) of each chunk
   float* gram;    // (B, nc, Q, Q): C_c B_c^T
-  float* yinter;  // (B, H, nc, 2, Q, P): sum_n C_t[n] H_c[p, n] over each half of the states
+  float* yinter;  // (B, H, nc, Q, P): sum_n C_t[n] H_c[p, n]
                   // (before the exp2(cum_t) factor)
   int64_t seqlen, heads;
   int nchunks;
@@ -231,21 +231,24 @@ __global__ __launch_bounds__(kThreads * HG) void ssd_state_kernel(SsdArgs a) {
 }
 
 // ---- recurrence over chunks and the incoming-state products -------------------------------
-// Grid (2 P / 16, H, B), 4 waves. A workgroup owns head channels p0 .. p0 + 15 of one (b, h) and
-// one half of the states, n0 .. n0 + 63, and walks the chunks in order with that block of the
-// state in registers. Every wave keeps the whole block (lane (g, i): channel p0 + i, states
-// n0 + 16 k + 4 g .. + 3 for k = 0..3), so the waves exchange nothing. For chunk c, wave w
-// contracts the C rows of tokens 16 w .. 16 w + 15 with H_c over the block's 64 states (A operand
-// C, B operand H^T, contraction index n0 + 16 k + 4 g + q at k-step (k, q), one accumulator per
-// q: a 16-byte load per lane and k reads 64 contiguous bytes of each row), writes these partial
-// products (the output kernel adds the two halves) to the workspace, and then advances the state:
-// H_{c+1} = exp(cum_last of c) H_c + S_c. The next chunk's C rows and S slice are loaded while
-// the current chunk is contracted (two register sets, chunks taken in pairs).
+// Grid (P / 16, H, B), 8 waves. A workgroup owns head channels p0 .. p0 + 15 of one (b, h) and
+// walks the chunks in order with that block of the state in registers: waves 0-3 hold states
+// 0 .. 63, waves 4-7 states 64 .. 127 (half = 0, 1; n0 = 64 half). Every wave of a half keeps
+// that half's whole block (lane (g, i): channel p0 + i, states n0 + 16 k + 4 g .. + 3 for
+// k = 0..3). For chunk c, wave w of a half contracts the C rows of tokens 16 w .. 16 w + 15 with
+// H_c over the half's 64 states (A operand C, B operand H^T, contraction index n0 + 16 k + 4 g + q
+// at k-step (k, q), one accumulator per q: a 16-byte load per lane and k reads 64 contiguous
+// bytes of each row) and advances the state: H_{c+1} = exp(cum_last of c) H_c + S_c. The upper
+// half leaves its products in LDS; after the chunk's barrier the lower half adds them to its own
+// and stores the sum, so the workspace holds one product per output. The next chunk's C rows and
+// S slice are loaded while the current chunk is contracted (two register sets, chunks taken in
+// pairs).
 template <typename Act>
-__global__ __launch_bounds__(kThreads) void ssd_carry_kernel(SsdArgs a) {
+__global__ __launch_bounds__(2 * kThreads) void ssd_carry_kernel(SsdArgs a) {
   const int64_t h = blockIdx.y, b = blockIdx.z;
-  const int p0 = 16 * static_cast<int>(blockIdx.x >> 1), half = blockIdx.x & 1, n0 = 64 * half;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
+  const int p0 = 16 * static_cast<int>(blockIdx.x);
+  const int tid = threadIdx.x, half = tid >> 8, ht = tid & 255, n0 = 64 * half;
+  const int lane = tid & 63, w = ht >> 6, g = lane >> 4, i = lane & 15;
   const int64_t bh = b * a.heads + h;
   const Act* Cp = static_cast<const Act*>(a.C);
   const int64_t srow = (bh * kP + p0 + i) * kN + n0 + 4 * g;  // this lane's part of a state
@@ -258,16 +261,19 @@ __global__ __launch_bounds__(kThreads) void ssd_carry_kernel(SsdArgs a) {
   }
   // Every wave has read its state before wave 0 may write state_out (which may be state_in).
   __syncthreads();
-  // S_c is read from memory once per workgroup: thread t loads 16 bytes of row p0 + t / 16 and
-  // stores them in LDS where lane (g, i) of every wave reads its k-th float4 (slot 64 k + lane),
-  // two chunk buffers alternating. (C rows go straight to registers: staged through LDS as well
-  // they took 64 us instead of 43 us at 1 x 2048 x 64 heads.)
-  __shared__ float4 ssh[2][4 * 64];
-  const int prow = tid >> 4, pch = tid & 15;
+  // S_c is read from memory once per workgroup: thread t of a half loads 16 bytes of row
+  // p0 + t / 16 of the half's block and stores them in LDS where lane (g, i) of every wave of the
+  // half reads its k-th float4 (slot 64 k + lane), two chunk buffers alternating. (C rows go
+  // straight to registers: staged through LDS as well they took 64 us instead of 43 us at
+  // 1 x 2048 x 64 heads.)
+  __shared__ float4 ssh[2][2][4 * 64];
+  // The upper half's products of a chunk, [chunk parity][wave][r][lane].
+  __shared__ float ysh[2][4][4][64];
+  const int prow = ht >> 4, pch = ht & 15;
   const float* Sg = a.states + bh * a.nchunks * int64_t(kP * kN) + (p0 + prow) * kN + n0 + 4 * pch;
   const int sdst = (pch >> 2) * 64 + 16 * (pch & 3) + prow;
-  float* Y0 = a.yinter + (bh * a.nchunks * 2 + half) * int64_t(kQ * kP) + (16 * w + 4 * g) * kP +
-              p0 + i;
+  float* Y0 = a.yinter + bh * a.nchunks * int64_t(kQ * kP) + (16 * w + 4 * g) * kP + p0 + i;
+  float yown[4];  // the lower half's products of the last chunk, until the upper half's are in
   const float* dec = a.decay + bh * a.nchunks;
   // A chunk's inputs: its C rows, this thread's part of its S block and its decay, loaded a chunk
   // ahead of use (the decay with them: loaded next to its use, its wait would also wait for the
@@ -283,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void ssd_carry_kernel(SsdArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) cr[k] = load4(Cp, row + 16 * k);
   };
-  auto chunk = [&](int c, const float4 (&cr)[4], float d, const float4* sb) {
+  auto chunk = [&](const float4 (&cr)[4], float d, const float4* sb, int buf) {
     float4 sr[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) sr[k] = sb[64 * k + lane];
@@ -297,9 +303,14 @@ __global__ __launch_bounds__(kThreads) void ssd_carry_kernel(SsdArgs a) {
       acc[2] = mfma4(cr[k].z, hs[4 * k + 2], acc[2]);
       acc[3] = mfma4(cr[k].w, hs[4 * k + 3], acc[3]);
     }
-    float* Y = Y0 + int64_t(c) * (2 * kQ * kP);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Y[r * kP] = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
+    for (int r = 0; r < 4; ++r) {
+      const float v = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
+      if (half)
+        ysh[buf][w][r][lane] = v;
+      else
+        yown[r] = v;
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       hs[4 * k] = fmaf(d, hs[4 * k], sr[k].x);
@@ -308,28 +319,40 @@ __global__ __launch_bounds__(kThreads) void ssd_carry_kernel(SsdArgs a) {
       hs[4 * k + 3] = fmaf(d, hs[4 * k + 3], sr[k].w);
     }
   };
+  // After the barrier that follows chunk c: the lower half stores the chunk's products.
+  auto finish = [&](int c, int buf) {
+    if (half == 0) {
+      float* Y = Y0 + int64_t(c) * (kQ * kP);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Y[r * kP] = yown[r] + ysh[buf][w][r][lane];
+    }
+  };
   float4 c0[4], c1[4], g0, g1;
   float d0, d1;
   // Prefetches past the last chunk reload the last chunk (unused), so no load sits behind a
   // branch; the scheduling barriers keep each prefetch ahead of the chunk it overlaps. Each
   // chunk's S block is in LDS before the chunk starts; the barrier after a buffer is filled also
-  // orders the previous reads of that buffer before its next fill.
+  // orders the previous reads of that buffer before its next fill. The same barriers order the
+  // upper half's products (ysh[c & 1]) before the lower half reads them, and that read before
+  // the upper half refills the buffer two chunks later.
   const int last = a.nchunks - 1;
   load(0, c0, g0, d0);
-  ssh[0][sdst] = g0;
+  ssh[0][half][sdst] = g0;
   __syncthreads();
   for (int c = 0; c < a.nchunks; c += 2) {
     load(c + 1 < last ? c + 1 : last, c1, g1, d1);
     __builtin_amdgcn_sched_barrier(0);
-    chunk(c, c0, d0, ssh[0]);
-    ssh[1][sdst] = g1;
+    chunk(c0, d0, ssh[0][half], 0);
+    ssh[1][half][sdst] = g1;
     __syncthreads();
+    finish(c, 0);
     if (c + 1 > last) break;
     load(c + 2 < last ? c + 2 : last, c0, g0, d0);
     __builtin_amdgcn_sched_barrier(0);
-    chunk(c + 1, c1, d1, ssh[1]);
-    ssh[0][sdst] = g0;
+    chunk(c1, d1, ssh[1][half], 1);
+    ssh[0][half][sdst] = g0;
     __syncthreads();
+    finish(c + 1, 1);
   }
   if (w == 0) {
 #pragma unroll
@@ -389,13 +412,13 @@ __global__ __launch_bounds__(kThreads) void ssd_output_kernel(SsdArgs a) {
   // The incoming-state products of this lane's outputs (token 16 w + 4 g + r, channel 16 pt + i).
   float yin[4][4];
   {
-    const float* Yi = a.yinter + (bh * a.nchunks + c) * int64_t(2 * kQ * kP) +
+    const float* Yi = a.yinter + (bh * a.nchunks + c) * int64_t(kQ * kP) +
                       (16 * w + 4 * g) * kP + i;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
-        yin[r][pt] = Yi[r * kP + 16 * pt] + Yi[kQ * kP + r * kP + 16 * pt];
+        yin[r][pt] = Yi[r * kP + 16 * pt];
   }
   __syncthreads();  // xs, cum_hi, cum_lo, dts ready
   f4 acc[4];
@@ -478,7 +501,7 @@ SsdPlan plan_ssd(const axon_ssd_shape* s) {
   p.off_decay = round_up(p.off_states + sizeof(float) * BH * p.nchunks * kP * kN, 256);
   p.off_gram = round_up(p.off_decay + sizeof(float) * BH * p.nchunks, 256);
   p.off_yinter = round_up(p.off_gram + sizeof(float) * size_t(s->batch) * p.nchunks * kQ * kQ, 256);
-  p.bytes = round_up(p.off_yinter + sizeof(float) * BH * p.nchunks * 2 * kQ * kP, 256);
+  p.bytes = round_up(p.off_yinter + sizeof(float) * BH * p.nchunks * kQ * kP, 256);
   return p;
 }
 
@@ -509,7 +532,7 @@ void launch_all(const SsdArgs& a, int64_t batch, hipStream_t st) {
                        a);
   else
     hipLaunchKernelGGL((ssd_state_kernel<Act, 1>), dim3(nc, H, B), blk, 0, st, a);
-  hipLaunchKernelGGL(ssd_carry_kernel<Act>, dim3(2 * kP / 16, H, B), blk, 0, st, a);
+  hipLaunchKernelGGL(ssd_carry_kernel<Act>, dim3(kP / 16, H, B), dim3(2 * kThreads), 0, st, a);
   hipLaunchKernelGGL(ssd_output_kernel<Act>, dim3(nc, H, B), blk, 0, st, a);
 }
 

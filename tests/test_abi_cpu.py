@@ -290,14 +290,14 @@ def _ssd(shape=None, params=None, ws_bytes=1 << 30, **over):
 
 def test_ssd_workspace_is_a_pure_function_of_shape():
     # (B, H, chunks, 64, 128) chunk states + (B, H, chunks) decays + (B, chunks, 64, 64) C B^T
-    # + (B, H, chunks, 2, 64, 64) incoming-state products, each rounded up to 256 bytes
+    # + (B, H, chunks, 64, 64) incoming-state products, each rounded up to 256 bytes
     n = A.ssd_workspace_bytes(_ssd_shape(batch=1, seqlen=2048, heads=64))
-    assert n == 64 * 32 * 64 * 128 * 4 + 64 * 32 * 4 + 32 * 64 * 64 * 4 + 64 * 32 * 2 * 64 * 64 * 4
+    assert n == 64 * 32 * 64 * 128 * 4 + 64 * 32 * 4 + 32 * 64 * 64 * 4 + 64 * 32 * 64 * 64 * 4
     n = A.ssd_workspace_bytes(_ssd_shape(batch=1, seqlen=2048, heads=63))
     assert n == (63 * 32 * 64 * 128 * 4 + 8192 + 32 * 64 * 64 * 4  # 63 * 32 * 4 rounds up
-                 + 63 * 32 * 2 * 64 * 64 * 4)
+                 + 63 * 32 * 64 * 64 * 4)
     assert A.ssd_workspace_bytes(_ssd_shape(seqlen=65, heads=1)) == (2 * 8192 * 4 + 256 +
-                                                                     2 * 4096 * 4 + 2 * 2 * 4096 * 4)
+                                                                     2 * 4096 * 4 + 2 * 4096 * 4)
     assert A.ssd_workspace_bytes(_ssd_shape(seqlen=0)) == 0
     assert A.ssd_workspace_bytes(_ssd_shape(head_dim=32)) == 0
     assert A.ssd_workspace_bytes(_ssd_shape(batch=0)) == 0
