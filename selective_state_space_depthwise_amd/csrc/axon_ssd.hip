@@ -153,12 +153,14 @@ __global__ __launch_bounds__(kThreads) void ssd_gram_kernel(SsdArgs a) {
 }
 
 // ---- S_c = x^T diag(w) B --------------------------------------------------------------------
-// Grid (nc, H / HG, B), 4 HG waves: HG heads of one chunk share the staged B. The chunk's x
-// (scaled by w_s = exp(cum_last - cum_s) dt_s) and B are staged in LDS. Wave w of a head computes
+// Grid (nc, H / HG, B), 4 HG waves: HG heads of one chunk share the staged B. The chunk's x and
+// B are staged in LDS while wave 0 of each head computes its weights w_s = exp(cum_last - cum_s)
+// dt_s (x is staged unscaled so that its loads need not wait for them). Wave w of a head computes
 // S^T for the head channels p = 16 w .. 16 w + 15 against all 8 blocks of 16 states, A operand
-// B^T (rows n), B operand the scaled x (columns p), contraction index s = 4 j + g; the result
-// D[n][p] leaves every lane 4 consecutive states of one channel, stored as one 16-byte write. Row strides of 80 and 144 floats put the four lane
-// groups of one LDS read in disjoint banks.
+// B^T (rows n), B operand x scaled by w_s as it is read (columns p), contraction index
+// s = 4 j + g; the result D[n][p] leaves every lane 4 consecutive states of one channel, stored
+// as one 16-byte write. Row strides of 80 and 144 floats put the four lane groups of one LDS read
+// in disjoint banks.
 constexpr int kXS = kP + 16;
 constexpr int kBS = kN + 16;
 
@@ -195,31 +197,26 @@ __global__ __launch_bounds__(kThreads * HG) void ssd_state_kernel(SsdArgs a) {
       *reinterpret_cast<float4*>(&bs[t * kBS + kPer * q + j]) = v;
     }
   }
-  __syncthreads();  // wsh ready
   {
-    // x of this thread's head: token (tid % 256) / 4, head channels 16 (tid % 4) .. + 15,
-    // scaled by w_s
     const Act* xp = static_cast<const Act*>(a.x);
     const int t = (tid & 255) >> 2, q = tid & 3;
     const int64_t tok = tok0 + t;
     const bool ok = tok < a.seqlen;
-    const float ws = wsh[hg][t];
 #pragma unroll
     for (int j = 0; j < 16; j += 4) {
-      float4 v = ok ? load4(xp, ((b * a.seqlen + tok) * a.heads + h) * kP + 16 * q + j)
-                    : float4{};
-      v.x *= ws, v.y *= ws, v.z *= ws, v.w *= ws;
+      const float4 v = ok ? load4(xp, ((b * a.seqlen + tok) * a.heads + h) * kP + 16 * q + j)
+                          : float4{};
       *reinterpret_cast<float4*>(&xs[hg][t * kXS + 16 * q + j]) = v;
     }
   }
-  __syncthreads();
+  __syncthreads();  // wsh, x and B ready
   f4 acc[8];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) acc[nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 4
   for (int j = 0; j < 16; ++j) {
     const int s = 4 * j + g;
-    const float xv = xs[hg][s * kXS + 16 * w + i];
+    const float xv = xs[hg][s * kXS + 16 * w + i] * wsh[hg][s];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[nt] = mfma4(bs[s * kBS + 16 * nt + i], xv, acc[nt]);
   }
