@@ -114,42 +114,47 @@ __device__ __forceinline__ float exp2_diff(float hi_a, float lo_a, float hi_b, f
 // a 16-lane row block 64 contiguous bytes per row.
 
 // ---- G_c = C_c B_c^T -----------------------------------------------------------------------
-// Grid (nc, B), 4 waves; wave w computes the 16-row block w against column blocks 0..w.
+// Grid (nc, B), 10 waves, one per 16 x 16 block of the lower block triangle: wave v takes row
+// block w and column block st <= w (v = w (w + 1) / 2 + st). Its C and B rows are loaded together
+// and the contraction over the 128 states runs as four independent accumulator chains (one per
+// jj), so a wave waits for one round of loads and its matrix instructions do not wait for each
+// other's results.
+constexpr int kGramWaves = 10;
+
 template <typename Act>
-__global__ __launch_bounds__(kThreads) void ssd_gram_kernel(SsdArgs a) {
+__global__ __launch_bounds__(64 * kGramWaves) void ssd_gram_kernel(SsdArgs a) {
   const int c = blockIdx.x;
   const int64_t b = blockIdx.y;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, i = lane & 15;
+  const int lane = threadIdx.x & 63, v = threadIdx.x >> 6, g = lane >> 4, i = lane & 15;
+  const int w = v < 1 ? 0 : v < 3 ? 1 : v < 6 ? 2 : 3;
+  const int st = v - w * (w + 1) / 2;
   const int64_t tok0 = int64_t(c) * kQ;
   const Act* Cp = static_cast<const Act*>(a.C);
   const Act* Bp = static_cast<const Act*>(a.B);
-  float4 crow[8];
+  float4 crow[8], brow[8];
   {
-    const int64_t tok = tok0 + 16 * w + i;
-    const bool ok = tok < a.seqlen;
-#pragma unroll
-    for (int jb = 0; jb < 8; ++jb)
-      crow[jb] = ok ? load4(Cp, (b * a.seqlen + tok) * kN + 16 * jb + 4 * g) : float4{};
-  }
-  float* G = a.gram + (b * a.nchunks + c) * int64_t(kQ * kQ);
-  for (int st = 0; st <= w; ++st) {
-    const int64_t tok = tok0 + 16 * st + i;
-    const bool ok = tok < a.seqlen;
-    float4 brow[8];
-#pragma unroll
-    for (int jb = 0; jb < 8; ++jb)
-      brow[jb] = ok ? load4(Bp, (b * a.seqlen + tok) * kN + 16 * jb + 4 * g) : float4{};
-    f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int64_t tc = tok0 + 16 * w + i, tb = tok0 + 16 * st + i;
+    const bool okc = tc < a.seqlen, okb = tb < a.seqlen;
 #pragma unroll
     for (int jb = 0; jb < 8; ++jb) {
-      acc = mfma4(crow[jb].x, brow[jb].x, acc);
-      acc = mfma4(crow[jb].y, brow[jb].y, acc);
-      acc = mfma4(crow[jb].z, brow[jb].z, acc);
-      acc = mfma4(crow[jb].w, brow[jb].w, acc);
+      crow[jb] = okc ? load4(Cp, (b * a.seqlen + tc) * kN + 16 * jb + 4 * g) : float4{};
+      brow[jb] = okb ? load4(Bp, (b * a.seqlen + tb) * kN + 16 * jb + 4 * g) : float4{};
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) G[(16 * w + 4 * g + r) * kQ + 16 * st + i] = acc[r];
   }
+  f4 acc[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) acc[jj] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int jb = 0; jb < 8; ++jb) {
+    acc[0] = mfma4(crow[jb].x, brow[jb].x, acc[0]);
+    acc[1] = mfma4(crow[jb].y, brow[jb].y, acc[1]);
+    acc[2] = mfma4(crow[jb].z, brow[jb].z, acc[2]);
+    acc[3] = mfma4(crow[jb].w, brow[jb].w, acc[3]);
+  }
+  float* G = a.gram + (b * a.nchunks + c) * int64_t(kQ * kQ);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    G[(16 * w + 4 * g + r) * kQ + 16 * st + i] = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
 }
 
 // ---- S_c = x^T diag(w) B --------------------------------------------------------------------
@@ -521,7 +526,7 @@ void launch_all(const SsdArgs& a, int64_t batch, hipStream_t st) {
   const dim3 blk(kThreads);
   const unsigned nc = static_cast<unsigned>(a.nchunks);
   const unsigned H = static_cast<unsigned>(a.heads), B = static_cast<unsigned>(batch);
-  hipLaunchKernelGGL(ssd_gram_kernel<Act>, dim3(nc, B), blk, 0, st, a);
+  hipLaunchKernelGGL(ssd_gram_kernel<Act>, dim3(nc, B), dim3(64 * kGramWaves), 0, st, a);
   // Two heads per workgroup where the head count allows (37.6 us against 44.8 us for one and
   // 41.0 us for four at 1 x 2048 x 64 heads: LDS then holds two workgroups per CU).
   if (H % 2 == 0)
