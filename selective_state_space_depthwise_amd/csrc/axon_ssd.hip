@@ -261,7 +261,8 @@ __global__ __launch_bounds__(2 * kThreads) void ssd_carry_kernel(SsdArgs a) {
                                 : float4{0.0f, 0.0f, 0.0f, 0.0f};
     hs[4 * k] = v.x, hs[4 * k + 1] = v.y, hs[4 * k + 2] = v.z, hs[4 * k + 3] = v.w;
   }
-  // Every wave has read its state before wave 0 may write state_out (which may be state_in).
+  // Every wave has read its state before the first wave of each half may write state_out (which
+  // may be state_in).
   __syncthreads();
   // S_c is read from memory once per workgroup: thread t of a half loads 16 bytes of row
   // p0 + t / 16 of the half's block and stores them in LDS where lane (g, i) of every wave of the
